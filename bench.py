@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused reduce + residual + RMSNorm (+fp8) epilogue on one MI355X.
+
+A step is one launch of the whole fused path (rank-order sum of N shard partials,
+residual add and store, RMSNorm and store, fp8 copy with per-token scales) over one
+batch of seeded synthetic input already resident in HBM. The default workload is the
+largest one: N=8 shards, 8192 tokens, hidden 16384, bf16, per-token fp8 (3.09 GB of
+algorithmic traffic per step).
+
+Prints ONE JSON line. ``value`` is algorithmic GB/s from the wall clock around the K
+timed steps; ``roofline.achieved`` uses the fused kernel's average duration from HIP
+events recorded on the stream it is launched on. ``cpu_baseline`` times the oracle on
+a bounded sample of the same workload on the host's cores.
+"""
+import argparse
+import hashlib
+import glob
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused reduce+residual+RMSNorm GB/s & tokens/s; fraction of HBM peak"
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "shard_reduce_residual_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload_name: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "fused_%s_counters.txt" % workload_name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        m = re.match(r"^\s*([a-z_]+)\s*:\s*(\S+)", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("source_digest") != source_digest() or "hbm_bytes_per_launch" not in kv:
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4", help="c0..c4 (default c4)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target oracle time for the CPU baseline (0: skip it)")
+    ap.add_argument("--no-copy-probe", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share of the fused epilogue; runs on more than "
+              "one GPU are not part of this build (asked for --gpus %d, WORLD_SIZE %d)"
+              % (args.gpus, world), file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import shard_reduce_residual_amd as arf
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t, h = w.tokens, w.hidden
+    adt = workloads.TORCH_DTYPES[w.act_dtype]
+    p, r, g = workloads.generate(w, dev)
+    rout = torch.empty((t, h), dtype=adt, device=dev)
+    nout = torch.empty((t, h), dtype=adt, device=dev)
+    q = torch.empty((t, h), dtype=torch.uint8, device=dev) if w.quant else None
+    sc_out = torch.empty((t,), dtype=torch.float32, device=dev) if w.quant == "per_token" else None
+    sc_in = None
+    if w.quant == "per_tensor":
+        # per-tensor scale of the first launch's own output is not the oracle's; for timing
+        # any positive scale exercises the same instructions
+        sc_in = torch.tensor([0.01], dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def step():
+        if w.quant is None:
+            arf.arf_reduce_add_rmsnorm(p, r, g, w.eps, residual_out=rout, norm_out=nout,
+                                       stream=stream)
+        else:
+            mode = arf.ARF_QUANT_PER_TOKEN if w.quant == "per_token" else arf.ARF_QUANT_PER_TENSOR
+            arf.arf_reduce_add_rmsnorm_quant(p, r, g, w.eps, q, mode, scale_in=sc_in,
+                                             scale_out=sc_out, residual_out=rout,
+                                             norm_out=nout, stream=stream)
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    B = w.algorithmic_bytes()
+    value = B / (ms_per_step * 1e-3) / 1e9
+    achieved = B / (kernel_ms * 1e-3) / 1e9
+    traffic = read_traffic(w.name)
+
+    # HBM ceiling probe: a streaming copy of 1 GiB with the same load/store forms
+    copy = None
+    if not args.no_copy_probe:
+        nb = 1 << 30
+        src = torch.empty(nb, dtype=torch.uint8, device=dev).random_(0, 256)
+        dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            arf.arf_stream_copy(dst, src, nb, stream=stream)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(10):
+            arf.arf_stream_copy(dst, src, nb, stream=stream)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy = 2 * nb / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
+        del src, dst
+
+    cpu = None
+    parity = None
+    if args.cpu_seconds > 0:
+        cpu, parity = cpu_baseline(args, w, p, r, g, rout, nout, q, sc_out, sc_in)
+
+    plan = arf.arf_get_plan(w.n_shards, t, h, {"bf16": 0, "f16": 1, "f32": 2}[w.partial_dtype])
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_shards": w.n_shards, "tokens": t, "hidden": h,
+                   "partial_dtype": w.partial_dtype, "act_dtype": w.act_dtype,
+                   "quant": w.quant, "algorithmic_bytes": B},
+        "tokens_per_s": round(t / (ms_per_step * 1e-3), 1),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "kernel_ms": round(kernel_ms, 5),
+        "plan": plan,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "hbm_copy_ceiling_GBs": None if copy is None else round(copy, 1),
+        "frac_of_copy_ceiling": None if copy is None else round(achieved / copy, 4),
+        "cpu_baseline": cpu,
+        "sample_parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(args, w, p, r, g, rout, nout, q, sc_out, sc_in):
+    """Oracle on the first rows of the same workload, on the host's cores, repeated until
+    about --cpu-seconds of work; also checks the GPU's outputs for those rows."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    rows = min(w.tokens, 1024)
+    ph = workloads.to_bits(p[:, :rows].contiguous())
+    rh = workloads.to_bits(r[:rows].contiguous())
+    gh = workloads.to_bits(g)
+    threads = min(16, oracle.default_threads())
+    kw = dict(partial_dtype=w.partial_dtype, act_dtype=w.act_dtype, quant=w.quant,
+              n_threads=threads)
+    if w.quant == "per_tensor":
+        kw["scale_in"] = float(sc_in.item())
+    oracle.lib()
+    passes, elapsed, ref = 0, 0.0, None
+    while elapsed < args.cpu_seconds and passes < 200:
+        s = time.perf_counter()
+        ref = oracle.reduce_add_rmsnorm(ph, rh, gh, w.eps, **kw)
+        elapsed += time.perf_counter() - s
+        passes += 1
+    sample_bytes = w.with_tokens(rows).algorithmic_bytes()
+    cpu = {"value": round(sample_bytes * passes / elapsed / 1e9, 3), "unit": "GB/s",
+           "tokens_per_s": round(rows * passes / elapsed, 1), "cores": threads,
+           "kind": "oracle",
+           "sample": "first %d of %d tokens of %s, %d passes, %.1f s"
+                     % (rows, w.tokens, w.name, passes, elapsed)}
+
+    def ordinal(b, bits):
+        b = b.astype(np.int64)
+        s = 1 << (bits - 1)
+        return np.where(b & s, -(b & (s - 1)), b)
+
+    gr = workloads.to_bits(rout[:rows])
+    gn = workloads.to_bits(nout[:rows])
+    par = {"rows": rows,
+           "residual_bit_exact": bool(np.array_equal(gr, ref["residual_out"])),
+           "norm_max_ulp": int(np.abs(ordinal(gn, 16) - ordinal(ref["norm_out"], 16)).max())}
+    if q is not None:
+        gq = q[:rows].cpu().numpy()
+        par["fp8_max_code_diff"] = int(np.abs(ordinal(gq, 8) - ordinal(ref["quant_out"], 8)).max())
+    return cpu, par
+
+
+if __name__ == "__main__":
+    sys.exit(main())

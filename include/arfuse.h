@@ -1,0 +1,161 @@
+/*
+ * arfuse.h -- C ABI of libarfuse: the fused epilogue of a tensor-parallel all-reduce on
+ * one MI355X (gfx950), at one GPU's share: N per-rank partial hidden states that are
+ * already resident in local HBM are summed in rank order, added to the residual,
+ * RMS-normalised, and written out (plus an optional OCP fp8-e4m3 copy).
+ *
+ * The operation is the one defined on the TensorRT-LLM page "allReduceFusionKernels.cu":
+ *   - allreduce_sum, fp32-accumulation branch (the default chosen by use_fp32_acc):
+ *     acc = float(p[0]); acc += float(p[r]) for r = 1..N-1; s = cast to the activation
+ *     type;
+ *   - fused_op / add128: r = s + residual_in, formed in the activation type; written
+ *     as residual_out;
+ *   - rms_norm: inv = 1/sqrt(sum(r^2)/hidden + eps); y = (r * inv) * gamma, cast to the
+ *     activation type; written as norm_out;
+ *   - the partials buffer is the oneshot-sync kernel's local receive buffer: shard r of
+ *     token t at offset (r*tokens + t)*hidden elements (also the FlashInfer page for
+ *     trtllm_create_ipc_workspace_for_all_reduce_fusion: tp_size x tokens x hidden
+ *     elements, 2-byte or, with use_fp32_lamport, 4-byte).
+ * The page's quantised output is a 4-bit format whose definition is not on the pages;
+ * this library writes OCP E4M3 codes instead (round to nearest even, saturating to
+ * +-448) of q = y * (1/scale), with a per-tensor scale given by the caller or a per-token
+ * scale max|y|/448 computed here.
+ *
+ * Conventions for every entry point below:
+ *   - Buffers are DEVICE pointers owned by the caller; the library allocates nothing,
+ *     keeps no state between calls (apart from a per-device compute-unit count and the
+ *     test-only override below) and never synchronises.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream). On ARF_OK exactly one
+ *     kernel has been enqueued on it (none when tokens == 0). Kernel faults surface at
+ *     the caller's next synchronisation, as usual in HIP.
+ *   - All arguments are validated before any HIP call: on any error status nothing is
+ *     enqueued and nothing is written. Sizes, types and eps are checked first; a call
+ *     with tokens == 0 is then complete (ARF_OK) and its pointers are not examined.
+ *   - Thread-safe and reentrant (arf_set_path_override excepted).
+ */
+#ifndef ARFUSE_H
+#define ARFUSE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ARF_VERSION 100 /* 0.1.0 */
+
+/* Element types (arguments typed int32_t take these values). */
+#define ARF_BF16 0
+#define ARF_F16 1
+#define ARF_F32 2
+
+/* fp8 scale modes. */
+#define ARF_QUANT_PER_TENSOR 0 /* y ~ code * scale_in[0], scale given by the caller */
+#define ARF_QUANT_PER_TOKEN 1  /* scale_out[t] = max_i |y[t][i]| / 448, written     */
+
+/* Limits. */
+#define ARF_MAX_SHARDS 16
+#define ARF_MAX_HIDDEN 65536
+
+typedef enum arf_status {
+    ARF_OK = 0,
+    ARF_ERR_NULL = 1,      /* a required pointer is NULL                                  */
+    ARF_ERR_SHAPE = 2,     /* n_shards not in 1..16, tokens < 0 or > 2^31-1, hidden not a
+                              positive multiple of 8 or above ARF_MAX_HIDDEN                */
+    ARF_ERR_DTYPE = 3,     /* act_dtype not BF16/F16, or partial_dtype neither act_dtype
+                              nor F32                                                      */
+    ARF_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned (scales: 4-byte)      */
+    ARF_ERR_ALIAS = 5,     /* an output overlaps another buffer (the only overlap allowed
+                              is residual_out == residual_in exactly)                      */
+    ARF_ERR_NO_OUTPUT = 6, /* residual_out and norm_out are both NULL (non-quant entry)    */
+    ARF_ERR_VALUE = 7,     /* eps negative or not finite; unknown quant mode; bad override */
+    ARF_ERR_HIP = 8        /* no usable device, or the kernel launch failed               */
+} arf_status;
+
+/*
+ * Fused rank-order reduce + residual add + RMSNorm.
+ *   partials      [n_shards][tokens][hidden] of partial_dtype, dense (shard stride
+ *                 tokens*hidden elements), 16-byte aligned.
+ *   n_shards      1..16 (the tensor-parallel degree).
+ *   tokens        rows, >= 0; 0 is a valid empty call (ARF_OK, nothing enqueued).
+ *   hidden        elements per row, a multiple of 8, at most ARF_MAX_HIDDEN.
+ *   partial_dtype ARF_F32 or act_dtype (fp32 partials are the page's fp32-buffer option).
+ *   act_dtype     ARF_BF16 or ARF_F16: type of residual_in/out, gamma and norm_out.
+ *   residual_in   [tokens][hidden], read.
+ *   residual_out  [tokens][hidden], written, nullable; may be equal to residual_in.
+ *   gamma         [hidden], read.
+ *   eps           >= 0 and finite, added to the mean of squares inside the root.
+ *   norm_out      [tokens][hidden], written, nullable.
+ * At least one of residual_out and norm_out must be non-NULL.
+ */
+arf_status arf_reduce_add_rmsnorm(const void* partials, int32_t n_shards, int64_t tokens,
+                                  int32_t hidden, int32_t partial_dtype, int32_t act_dtype,
+                                  const void* residual_in, void* residual_out,
+                                  const void* gamma, float eps, void* norm_out,
+                                  void* stream);
+
+/*
+ * The same, plus the fp8 copy of the normalised output (the page's quantised-output
+ * pattern, with OCP E4M3 in place of its 4-bit format):
+ *   residual_out, norm_out  nullable, both may be NULL.
+ *   quant_out  [tokens][hidden] uint8 E4M3 codes of y * (1/scale), written, required.
+ *   mode       ARF_QUANT_PER_TENSOR: scale_in (device, 1 float) is read; scale_out is
+ *              ignored and may be NULL. A scale that is not > 0 gives all-zero codes.
+ *              ARF_QUANT_PER_TOKEN: scale_out (device, [tokens] floats) receives
+ *              max|y[t]|/448 per token; scale_in is ignored and may be NULL.
+ */
+arf_status arf_reduce_add_rmsnorm_quant(const void* partials, int32_t n_shards,
+                                        int64_t tokens, int32_t hidden,
+                                        int32_t partial_dtype, int32_t act_dtype,
+                                        const void* residual_in, void* residual_out,
+                                        const void* gamma, float eps, void* norm_out,
+                                        uint8_t* quant_out, int32_t mode,
+                                        const float* scale_in, float* scale_out,
+                                        void* stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* arf_status_string(int32_t status);
+
+/* ARF_VERSION of the loaded library. */
+int32_t arf_version(void);
+
+/*
+ * Launch geometry that a call with these sizes would use, without a device call when
+ * num_cus > 0 (num_cus <= 0: the current device's compute-unit count is queried, which
+ * may return ARF_ERR_HIP). out[0] = path (1 row per wavefront, 2 row per workgroup),
+ * out[1] = wavefronts per workgroup, out[2] = 16-byte chunks (8 elements) per lane,
+ * out[3] = workgroups in the grid. Honours arf_set_path_override.
+ */
+arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
+                        int32_t partial_dtype, int32_t num_cus, int32_t* out);
+
+/*
+ * TEST AND TUNING ONLY; process-wide, not to be changed while other threads call the
+ * library. path 0 = automatic (the other two arguments must be 0); 1 = one row per
+ * wavefront; 2 = one row per workgroup. waves_per_block (1 row per workgroup only:
+ * 2, 4, 8 or 16) and chunks_per_lane (1, 2, 4 or 8) force the geometry when non-zero.
+ * A forced geometry that cannot cover a call's hidden size makes that call return
+ * ARF_ERR_VALUE. Returns ARF_ERR_VALUE for values outside these sets.
+ */
+arf_status arf_set_path_override(int32_t path, int32_t waves_per_block,
+                                 int32_t chunks_per_lane);
+
+/*
+ * The quantiser's conversion alone, for testing it: out[i] = E4M3 code of in[i], round
+ * to nearest even, saturating to +-448, NaN -> S.1111.111 (OCP OFP8 E4M3). in and out
+ * are device pointers (in 4-byte aligned), n >= 0 elements. One kernel on `stream`.
+ */
+arf_status arf_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream);
+
+/*
+ * Streaming copy of `bytes` bytes (a multiple of 16; both pointers 16-byte aligned, the
+ * ranges must not overlap) with the same load/store forms as the fused kernel: the
+ * measured HBM ceiling and the calibration kernel for the byte counters.
+ */
+arf_status arf_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARFUSE_H */

@@ -1,0 +1,150 @@
+"""Python binding of libarfuse (argument marshalling only).
+
+Every step of the fused reduce + residual + RMSNorm (+fp8) path runs in the HIP
+kernels of ``libarfuse.so``; this module only turns torch tensors into device pointers,
+sizes and a stream handle, calls the C ABI declared in ``include/arfuse.h`` and turns a
+non-zero status into an exception. There is no fallback: if the library is missing the
+import of a function raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libarfuse.so")
+
+ARF_BF16, ARF_F16, ARF_F32 = 0, 1, 2
+ARF_QUANT_PER_TENSOR, ARF_QUANT_PER_TOKEN = 0, 1
+ARF_MAX_SHARDS, ARF_MAX_HIDDEN = 16, 65536
+STATUS = ["ARF_OK", "ARF_ERR_NULL", "ARF_ERR_SHAPE", "ARF_ERR_DTYPE", "ARF_ERR_ALIGN",
+          "ARF_ERR_ALIAS", "ARF_ERR_NO_OUTPUT", "ARF_ERR_VALUE", "ARF_ERR_HIP"]
+
+# Exported symbols and their C signatures (kept in step with include/arfuse.h).
+_vp, _i32, _i64, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+SIGNATURES = {
+    "arf_reduce_add_rmsnorm": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _f32,
+                                      _vp, _vp]),
+    "arf_reduce_add_rmsnorm_quant": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp,
+                                            _f32, _vp, _vp, _i32, _vp, _vp, _vp]),
+    "arf_status_string": (ctypes.c_char_p, [_i32]),
+    "arf_version": (_i32, []),
+    "arf_get_plan": (_i32, [_i32, _i64, _i32, _i32, _i32, ctypes.POINTER(_i32)]),
+    "arf_set_path_override": (_i32, [_i32, _i32, _i32]),
+    "arf_e4m3_encode": (_i32, [_vp, _vp, _i64, _vp]),
+    "arf_stream_copy": (_i32, [_vp, _vp, _i64, _vp]),
+}
+
+
+class ArfError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        name = STATUS[status] if 0 <= status < len(STATUS) else str(status)
+        super().__init__("%s returned %s" % (where, name))
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libarfuse.so (built by ``shard_reduce_residual_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libarfuse.so is not built (%s); run "
+                              "`python -m shard_reduce_residual_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.bfloat16: ARF_BF16, torch.float16: ARF_F16, torch.float32: ARF_F32}
+    if t.dtype not in codes:
+        raise TypeError("unsupported dtype %s" % t.dtype)
+    return codes[t.dtype]
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise ArfError(st, where)
+
+
+def arf_reduce_add_rmsnorm(partials, residual_in, gamma, eps: float, residual_out=None,
+                           norm_out=None, stream=None) -> None:
+    """partials [N][T][H] (bf16/f16, or f32); residual_in/_out, norm_out [T][H] and
+    gamma [H] in the activation type. Enqueues one kernel on ``stream``."""
+    n, t, h = partials.shape
+    st = lib().arf_reduce_add_rmsnorm(_ptr(partials), n, t, h, _dtype_code(partials),
+                                      _dtype_code(residual_in), _ptr(residual_in),
+                                      _ptr(residual_out), _ptr(gamma), float(eps),
+                                      _ptr(norm_out), _stream(stream))
+    _check(st, "arf_reduce_add_rmsnorm")
+
+
+def arf_reduce_add_rmsnorm_quant(partials, residual_in, gamma, eps: float, quant_out,
+                                 mode: int, scale_in=None, scale_out=None,
+                                 residual_out=None, norm_out=None, stream=None) -> None:
+    """As arf_reduce_add_rmsnorm plus ``quant_out`` [T][H] uint8 E4M3 codes;
+    ``mode`` ARF_QUANT_PER_TENSOR (``scale_in``: 1-element f32 device tensor) or
+    ARF_QUANT_PER_TOKEN (``scale_out``: [T] f32 device tensor, written)."""
+    n, t, h = partials.shape
+    st = lib().arf_reduce_add_rmsnorm_quant(
+        _ptr(partials), n, t, h, _dtype_code(partials), _dtype_code(residual_in),
+        _ptr(residual_in), _ptr(residual_out), _ptr(gamma), float(eps), _ptr(norm_out),
+        _ptr(quant_out), int(mode), _ptr(scale_in), _ptr(scale_out), _stream(stream))
+    _check(st, "arf_reduce_add_rmsnorm_quant")
+
+
+def arf_status_string(status: int) -> str:
+    return lib().arf_status_string(status).decode()
+
+
+def arf_version() -> int:
+    return lib().arf_version()
+
+
+def arf_get_plan(n_shards: int, tokens: int, hidden: int, partial_dtype: int,
+                 num_cus: int = 0) -> dict:
+    out = (_i32 * 4)()
+    _check(lib().arf_get_plan(n_shards, tokens, hidden, partial_dtype, num_cus, out),
+           "arf_get_plan")
+    return {"path": out[0], "waves": out[1], "chunks": out[2], "grid": out[3]}
+
+
+def arf_set_path_override(path: int, waves_per_block: int = 0, chunks_per_lane: int = 0):
+    _check(lib().arf_set_path_override(path, waves_per_block, chunks_per_lane),
+           "arf_set_path_override")
+
+
+def arf_e4m3_encode(x, out, stream=None) -> None:
+    _check(lib().arf_e4m3_encode(_ptr(x), _ptr(out), x.numel(), _stream(stream)),
+           "arf_e4m3_encode")
+
+
+def arf_stream_copy(dst, src, nbytes: int | None = None, stream=None) -> None:
+    nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check(lib().arf_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)),
+           "arf_stream_copy")

@@ -1,0 +1,339 @@
+// arfuse_device.hpp -- gfx950 device code of libarfuse.
+//
+// One fused, single-pass kernel: every byte of the partials and the residual is read
+// from HBM once, every output is written once. The method (TensorRT-LLM page
+// "allReduceFusionKernels.cu": allreduce_sum fp32 branch, fused_op/add128, rms_norm;
+// oneshot-sync post-barrier loop for the [N][tokens][hidden] layout) is reproduced in
+// its rounding order: fp32 rank-order sum -> cast to the activation type -> residual add
+// in the activation type -> mean of squares -> (x * inv) * gamma -> cast.
+//
+// Design for CDNA4 (not a translation of the page's cluster/DSMEM kernel):
+//  * A row (token) belongs to one wavefront (small hidden) or one workgroup (large
+//    hidden); the page needed up to 8 cooperating CTAs per token, here one workgroup of
+//    up to 16 wave64s covers hidden = 65536.
+//  * Each lane owns C 16-byte chunks (8 elements) at chunk index j*G + lane (G lanes per
+//    row), so each load instruction of a wavefront covers 1 KiB of contiguous HBM.
+//  * All global traffic uses raw buffer instructions with a per-row resource whose size
+//    is the row's bytes: lanes past the end of a ragged row read zeros and their stores
+//    are dropped by the hardware range check, so there is no tail branch.
+//  * Streaming data (partials, residual, outputs) carries the non-temporal hint; gamma is
+//    shared by all rows and uses the default policy.
+//  * The mean of squares is accumulated in fp64 per lane (squares of 16-bit values are
+//    exact in fp64), reduced across the wavefront with cross-lane shuffles and across
+//    wavefronts through LDS in a fixed order, so the result does not depend on timing.
+//  * The normalised row stays in registers (packed 16-bit) between the two reductions of
+//    the per-token fp8 scale, so nothing is re-read from HBM.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace arf {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Resource word 3 for raw (untyped, stride 0) buffers on gfx9-family GPUs: data format
+// 32 bits, no swizzle. With stride 0 the range check compares the byte offset against
+// the record count, which is how ragged rows are handled.
+constexpr int kBufferWord3 = 0x00020000;
+// Cache-policy operand of the buffer builtins on gfx940-family GPUs: bit 1 = NT.
+constexpr int kAuxStream = 2;
+constexpr int kAuxDefault = 0;
+
+enum QuantMode : int32_t { kQuantNone = 0, kQuantTensor = 1, kQuantToken = 2 };
+
+struct Params {
+    const void* partials;
+    const void* residual_in;
+    void* residual_out;   // nullable
+    const void* gamma;
+    void* norm_out;       // nullable
+    uint8_t* quant_out;   // used when quant_mode != kQuantNone
+    const float* scale_in;
+    float* scale_out;
+    int64_t tokens;
+    int32_t hidden;
+    int32_t n_shards;
+    float eps;
+    int32_t quant_mode;
+};
+
+struct ActBF16 {};
+struct ActF16 {};
+struct PartF32 {};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kBufferWord3);
+}
+
+// ---- 16-bit <-> fp32 -----------------------------------------------------------------
+
+__device__ __forceinline__ void unpack8(ActBF16, u32x4 v, float f[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(v[i] << 16);
+        f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+    }
+}
+
+// The halves are taken with integer shifts: bit-casting a vector element to a half2
+// vector here was compiled into a load of the first dword only (hipcc of ROCm 7.2).
+__device__ __forceinline__ void unpack8(ActF16, u32x4 v, float f[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w = v[i];
+        f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+        f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    }
+}
+
+// fp32 -> 16-bit, round to nearest even (gfx950 converts bf16 pairs in one instruction).
+__device__ __forceinline__ u32x4 pack8(ActBF16, const float f[8]) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f32x2 a = {f[2 * i], f[2 * i + 1]};
+        v[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2));
+    }
+    return v;
+}
+
+__device__ __forceinline__ u32x4 pack8(ActF16, const float f[8]) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f32x2 a = {f[2 * i], f[2 * i + 1]};
+        v[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, f16x2));
+    }
+    return v;
+}
+
+// ---- fp32 -> OCP E4M3 ------------------------------------------------------------------
+// Magnitudes above 448 are clamped first (saturating conversion; NaN is kept), then the
+// hardware converter rounds to nearest even. Four values -> one dword, lowest byte first.
+__device__ __forceinline__ float e4m3_sat(float v) {
+    float c = __builtin_fabsf(v) <= 448.0f ? v : __builtin_copysignf(448.0f, v);
+    return v != v ? v : c;
+}
+
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(a), e4m3_sat(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(c), e4m3_sat(d), w, true);
+    return (uint32_t)w;
+}
+
+// ---- cross-lane reductions (wave64) ------------------------------------------------------
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+// ---- the fused kernel -------------------------------------------------------------------
+//
+// PT: partial element type tag (ActBF16 / ActF16 / PartF32); AT: activation tag.
+// NMAX: compile-time upper bound of n_shards (shards r >= n_shards are skipped by a
+// uniform branch). C: chunks per lane. WAVES: wavefronts per workgroup. ROW_PER_WAVE:
+// each wavefront owns one row (else the whole workgroup owns one row).
+template <class PT> struct PartTraits {
+    static constexpr int kPieces = 1;   // 16-byte loads per chunk per shard
+    static constexpr int kBytes = 2;
+};
+template <> struct PartTraits<PartF32> {
+    static constexpr int kPieces = 2;
+    static constexpr int kBytes = 4;
+};
+
+template <class AT>
+__device__ __forceinline__ void load_partial_chunk(AT, u32x4 const (&v)[1], float f[8]) {
+    unpack8(AT{}, v[0], f);
+}
+template <class AT>
+__device__ __forceinline__ void load_partial_chunk(AT, u32x4 const (&v)[2], float f[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[i] = __uint_as_float(v[0][i]);
+        f[4 + i] = __uint_as_float(v[1][i]);
+    }
+}
+
+template <class PT, class AT, int NMAX, int C, int WAVES, bool ROW_PER_WAVE>
+__global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p) {
+    constexpr int PW = PartTraits<PT>::kPieces;
+    constexpr int G = ROW_PER_WAVE ? 64 : WAVES * 64;   // lanes per row
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+
+    int64_t row;
+    int gl;
+    if constexpr (ROW_PER_WAVE) {
+        row = (int64_t)blockIdx.x * WAVES + __builtin_amdgcn_readfirstlane(wave);
+        if (row >= p.tokens) return;   // whole wavefront leaves; no workgroup barrier here
+        gl = lane;
+    } else {
+        row = blockIdx.x;
+        gl = threadIdx.x;
+    }
+
+    const uint32_t H = (uint32_t)p.hidden;
+    const int n = p.n_shards;
+    const uint32_t act_row = H * 2u;
+    const uint32_t part_row = H * (uint32_t)PartTraits<PT>::kBytes;
+    const int64_t act_off = row * (int64_t)act_row;
+
+    const auto r_in = make_rsrc((const char*)p.residual_in + act_off, act_row);
+    const auto r_out = make_rsrc((char*)p.residual_out + act_off, p.residual_out ? act_row : 0u);
+    const auto y_out = make_rsrc((char*)p.norm_out + act_off, p.norm_out ? act_row : 0u);
+    const auto g_in = make_rsrc(p.gamma, act_row);
+
+    __amdgpu_buffer_rsrc_t part[NMAX];
+#pragma unroll
+    for (int r = 0; r < NMAX; ++r)
+        part[r] = make_rsrc((const char*)p.partials +
+                                ((int64_t)r * p.tokens + row) * (int64_t)part_row,
+                            part_row);
+
+    // ---- pass over HBM: rank-order sum, cast, residual add, cast, store, sum of squares
+    double ss = 0.0;
+    u32x4 xr[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+        const uint32_t chunk = (uint32_t)(j * G + gl);
+        const uint32_t off_a = chunk * 16u;
+        const uint32_t off_p = chunk * 16u * PW;
+        u32x4 pv[NMAX][PW];
+#pragma unroll
+        for (int r = 0; r < NMAX; ++r) {
+            if (r < n) {
+#pragma unroll
+                for (int w = 0; w < PW; ++w)
+                    pv[r][w] = __builtin_amdgcn_raw_buffer_load_b128(part[r], off_p + 16u * w,
+                                                                     0, kAuxStream);
+            }
+        }
+        const u32x4 rv = __builtin_amdgcn_raw_buffer_load_b128(r_in, off_a, 0, kAuxStream);
+
+        float acc[8];
+        load_partial_chunk(AT{}, pv[0], acc);
+#pragma unroll
+        for (int r = 1; r < NMAX; ++r) {
+            if (r < n) {
+                float t[8];
+                load_partial_chunk(AT{}, pv[r], t);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = acc[e] + t[e];
+            }
+        }
+        float s[8], res[8], sum[8];
+        unpack8(AT{}, pack8(AT{}, acc), s);      // reduced value in the activation type
+        unpack8(AT{}, rv, res);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum[e] = s[e] + res[e];
+        const u32x4 rr = pack8(AT{}, sum);       // residual_out
+        __builtin_amdgcn_raw_buffer_store_b128(rr, r_out, off_a, 0, kAuxStream);
+        xr[j] = rr;
+        float x[8];
+        unpack8(AT{}, rr, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = __builtin_fma((double)x[e], (double)x[e], ss);
+    }
+
+    u32x4 gv[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+        gv[j] = __builtin_amdgcn_raw_buffer_load_b128(g_in, (uint32_t)(j * G + gl) * 16u, 0,
+                                                      kAuxDefault);
+
+    // ---- mean of squares across the row
+    ss = wave_sum(ss);
+    if constexpr (!ROW_PER_WAVE) {
+        __shared__ double s_ss[WAVES];
+        if (lane == 0) s_ss[wave] = ss;
+        __syncthreads();
+        ss = 0.0;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) ss += s_ss[w];
+    }
+    const float inv = (float)(1.0 / __builtin_sqrt(ss / (double)H + (double)p.eps));
+
+    // ---- normalise, store, and keep the cast result for the fp8 copy
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+        float x[8], g[8], y[8];
+        unpack8(AT{}, xr[j], x);
+        unpack8(AT{}, gv[j], g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = x[e] * inv;
+            y[e] = v * g[e];
+        }
+        const u32x4 yr = pack8(AT{}, y);
+        __builtin_amdgcn_raw_buffer_store_b128(yr, y_out, (uint32_t)(j * G + gl) * 16u, 0,
+                                               kAuxStream);
+        xr[j] = yr;
+        if (p.quant_mode == kQuantToken) {
+            float yc[8];
+            unpack8(AT{}, yr, yc);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, __builtin_fabsf(yc[e]));
+        }
+    }
+    if (p.quant_mode == kQuantNone) return;
+
+    // ---- fp8 copy: q = E4M3(y * (1/scale))
+    float scale;
+    if (p.quant_mode == kQuantToken) {
+        amax = wave_max(amax);
+        if constexpr (!ROW_PER_WAVE) {
+            __shared__ float s_max[WAVES];
+            if (lane == 0) s_max[wave] = amax;
+            __syncthreads();
+            amax = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) amax = fmaxf(amax, s_max[w]);
+        }
+        scale = amax / 448.0f;
+        if (gl == 0) p.scale_out[row] = scale;
+    } else {
+        scale = p.scale_in[0];
+    }
+    const float inv_scale = scale > 0.0f ? 1.0f / scale : 0.0f;
+    const auto q_out = make_rsrc(p.quant_out + row * (int64_t)H, H);
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+        float y[8];
+        unpack8(AT{}, xr[j], y);
+        u32x2 q;
+        q[0] = e4m3x4(y[0] * inv_scale, y[1] * inv_scale, y[2] * inv_scale, y[3] * inv_scale);
+        q[1] = e4m3x4(y[4] * inv_scale, y[5] * inv_scale, y[6] * inv_scale, y[7] * inv_scale);
+        __builtin_amdgcn_raw_buffer_store_b64(q, q_out, (uint32_t)(j * G + gl) * 8u, 0,
+                                              kAuxStream);
+    }
+}
+
+// Host-side launcher for one instantiation; returns the launch's own status.
+template <class PT, class AT, int NMAX, int C, int WAVES, bool ROW_PER_WAVE>
+hipError_t launch_fused(const Params& p, uint32_t grid, hipStream_t stream) {
+    Params arg = p;
+    void* args[] = {&arg};
+    return hipLaunchKernel(
+        reinterpret_cast<const void*>(&fused_reduce_add_rmsnorm<PT, AT, NMAX, C, WAVES, ROW_PER_WAVE>),
+        dim3(grid), dim3(WAVES * 64), args, 0, stream);
+}
+
+typedef hipError_t (*launch_fn)(const Params&, uint32_t, hipStream_t);
+
+}  // namespace arf

@@ -1,0 +1,370 @@
+// arfuse_host.hip -- the C ABI of libarfuse: argument validation, launch geometry and
+// dispatch to the instantiated fused kernel, plus the two utility entry points (the
+// quantiser's conversion alone, and a streaming copy for the HBM ceiling).
+//
+// Every argument is validated before the first HIP call. The only device queries are
+// hipGetDevice and the compute-unit count (cached per device).
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "arfuse.h"
+#include "arfuse_table.hpp"
+
+namespace {
+
+using arf::launch_fn;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];   // 0 = not queried yet
+std::atomic<int> g_path{0}, g_waves{0}, g_chunks{0};
+
+struct Plan {
+    int path;      // 1 row per wavefront, 2 row per workgroup
+    int waves;     // wavefronts per workgroup
+    int chunks;    // 16-byte chunks per lane
+    uint32_t grid; // workgroups
+};
+
+bool in_menu_c(int c) { return c == 1 || c == 2 || c == 4 || c == 8; }
+bool in_menu_w(int w) { return w == 2 || w == 4 || w == 8 || w == 16; }
+
+// Launch geometry. hidden/8 chunks per row are spread over the lanes that own the row.
+//  * one row per wavefront (4 wavefronts per workgroup) when a wavefront covers the row
+//    with at most 8 chunks per lane and there are enough rows to give every compute unit
+//    several workgroups;
+//  * otherwise one row per workgroup. With many rows (at least 2 per compute unit) each
+//    lane takes several chunks so that a workgroup stays small (about 4 wavefronts) and
+//    several rows share a compute unit; with few rows the row is spread over as many
+//    wavefronts as possible (one chunk per lane) to expose parallelism.
+arf_status make_plan(int64_t tokens, int32_t hidden, int num_cus, Plan* pl) {
+    const int hc = hidden / 8;
+    int path = g_path.load(), waves = g_waves.load(), chunks = g_chunks.load();
+    if (path == 0) {
+        const bool enough_rows = tokens >= 8LL * num_cus;
+        path = (hc <= 64 * 8 && enough_rows) ? 1 : 2;
+        waves = chunks = 0;
+    }
+    if (path == 1) {
+        waves = 4;
+        if (chunks == 0) {
+            for (chunks = 1; chunks < 8 && 64 * chunks < hc; chunks *= 2) {}
+        }
+        if (64 * chunks < hc) return ARF_ERR_VALUE;
+        pl->grid = (uint32_t)((tokens + 3) / 4);
+    } else {
+        if (waves && chunks) {
+            // forced
+        } else if (chunks) {
+            for (waves = 2; waves < 16 && waves * 64 * chunks < hc; waves *= 2) {}
+        } else if (waves) {
+            for (chunks = 1; chunks < 8 && waves * 64 * chunks < hc; chunks *= 2) {}
+        } else if (tokens >= 2LL * num_cus) {
+            for (chunks = 1; chunks < 8 && 4 * 64 * chunks < hc; chunks *= 2) {}
+            for (waves = 2; waves < 16 && waves * 64 * chunks < hc; waves *= 2) {}
+        } else {
+            for (chunks = 1; chunks < 8 && 16 * 64 * chunks < hc; chunks *= 2) {}
+            for (waves = 2; waves < 16 && waves * 64 * chunks < hc; waves *= 2) {}
+        }
+        if (waves * 64 * chunks < hc) return ARF_ERR_VALUE;
+        pl->grid = (uint32_t)tokens;
+    }
+    pl->path = path;
+    pl->waves = waves;
+    pl->chunks = chunks;
+    return ARF_OK;
+}
+
+int nmax_for(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 8 ? 8 : 16; }
+
+launch_fn lookup(int pdt, int adt, int nmax, const Plan& pl) {
+    const bool rpw = pl.path == 1;
+    if (adt == ARF_BF16) {
+        return pdt == ARF_F32 ? arf::lookup_f32_bf16(nmax, rpw, pl.waves, pl.chunks)
+                              : arf::lookup_bf16_bf16(nmax, rpw, pl.waves, pl.chunks);
+    }
+    return pdt == ARF_F32 ? arf::lookup_f32_f16(nmax, rpw, pl.waves, pl.chunks)
+                          : arf::lookup_f16_f16(nmax, rpw, pl.waves, pl.chunks);
+}
+
+arf_status device_cus(int* cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ARF_ERR_HIP;
+    if (dev < kMaxDevices) {
+        int c = g_cu_count[dev].load(std::memory_order_relaxed);
+        if (c > 0) { *cus = c; return ARF_OK; }
+    }
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        c <= 0)
+        return ARF_ERR_HIP;
+    if (dev < kMaxDevices) g_cu_count[dev].store(c, std::memory_order_relaxed);
+    *cus = c;
+    return ARF_OK;
+}
+
+struct Range {
+    uintptr_t b, e;
+};
+Range span(const void* p, int64_t bytes) {
+    return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+bool overlap(Range a, Range b) { return a.b < b.e && b.b < a.e; }
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+struct Call {
+    const void* partials;
+    int32_t n;
+    int64_t tokens;
+    int32_t hidden;
+    int32_t pdt, adt;
+    const void* residual_in;
+    void* residual_out;
+    const void* gamma;
+    float eps;
+    void* norm_out;
+    uint8_t* quant_out;
+    int32_t quant;   // arf::QuantMode
+    const float* scale_in;
+    float* scale_out;
+};
+
+// Order: sizes, types and eps first; an empty call (tokens == 0) is then complete, so
+// its pointers may be NULL (zero-size tensors often have no address); otherwise
+// pointers, alignment and overlaps.
+arf_status validate(const Call& c) {
+    if (c.n < 1 || c.n > ARF_MAX_SHARDS || c.tokens < 0 || c.tokens > INT32_MAX ||
+        c.hidden <= 0 || c.hidden % 8 != 0 || c.hidden > ARF_MAX_HIDDEN)
+        return ARF_ERR_SHAPE;
+    if (c.adt != ARF_BF16 && c.adt != ARF_F16) return ARF_ERR_DTYPE;
+    if (c.pdt != c.adt && c.pdt != ARF_F32) return ARF_ERR_DTYPE;
+    if (!(c.eps >= 0.0f) || std::isinf(c.eps)) return ARF_ERR_VALUE;
+    if (c.tokens == 0) return ARF_OK;
+    if (!c.partials || !c.residual_in || !c.gamma) return ARF_ERR_NULL;
+    if (c.quant == arf::kQuantTensor && (!c.quant_out || !c.scale_in)) return ARF_ERR_NULL;
+    if (c.quant == arf::kQuantToken && (!c.quant_out || !c.scale_out)) return ARF_ERR_NULL;
+    if (c.quant == arf::kQuantNone && !c.residual_out && !c.norm_out) return ARF_ERR_NO_OUTPUT;
+    const void* t16[] = {c.partials, c.residual_in, c.residual_out, c.gamma, c.norm_out,
+                         c.quant_out};
+    for (const void* p : t16)
+        if (p && !aligned(p, 16)) return ARF_ERR_ALIGN;
+    if ((c.quant == arf::kQuantTensor && !aligned(c.scale_in, 4)) ||
+        (c.quant == arf::kQuantToken && !aligned(c.scale_out, 4)))
+        return ARF_ERR_ALIGN;
+
+    const int64_t th = c.tokens * (int64_t)c.hidden;
+    const int64_t sp = c.pdt == ARF_F32 ? 4 : 2;
+    Range in_part = span(c.partials, (int64_t)c.n * th * sp);
+    Range in_res = span(c.residual_in, th * 2);
+    Range in_gam = span(c.gamma, (int64_t)c.hidden * 2);
+    Range in_sc = c.quant == arf::kQuantTensor ? span(c.scale_in, 4) : Range{0, 0};
+    Range outs[4] = {
+        c.residual_out ? span(c.residual_out, th * 2) : Range{0, 0},
+        c.norm_out ? span(c.norm_out, th * 2) : Range{0, 0},
+        c.quant != arf::kQuantNone ? span(c.quant_out, th) : Range{0, 0},
+        c.quant == arf::kQuantToken ? span(c.scale_out, c.tokens * 4) : Range{0, 0},
+    };
+    for (int i = 0; i < 4; ++i) {
+        const Range o = outs[i];
+        if (o.b == o.e) continue;
+        if (overlap(o, in_part) || overlap(o, in_gam) || overlap(o, in_sc)) return ARF_ERR_ALIAS;
+        const bool in_place = i == 0 && c.residual_out == c.residual_in;
+        if (!in_place && overlap(o, in_res)) return ARF_ERR_ALIAS;
+        for (int k = i + 1; k < 4; ++k)
+            if (outs[k].b != outs[k].e && overlap(o, outs[k])) return ARF_ERR_ALIAS;
+    }
+    return ARF_OK;
+}
+
+arf_status run(const Call& c, void* stream) {
+    arf_status st = validate(c);
+    if (st != ARF_OK || c.tokens == 0) return st;
+    int cus = 0;
+    if ((st = device_cus(&cus)) != ARF_OK) return st;
+    Plan pl;
+    if ((st = make_plan(c.tokens, c.hidden, cus, &pl)) != ARF_OK) return st;
+    launch_fn fn = lookup(c.pdt, c.adt, nmax_for(c.n), pl);
+    if (!fn) return ARF_ERR_VALUE;
+    arf::Params p;
+    p.partials = c.partials;
+    p.residual_in = c.residual_in;
+    p.residual_out = c.residual_out;
+    p.gamma = c.gamma;
+    p.norm_out = c.norm_out;
+    p.quant_out = c.quant_out;
+    p.scale_in = c.scale_in;
+    p.scale_out = c.scale_out;
+    p.tokens = c.tokens;
+    p.hidden = c.hidden;
+    p.n_shards = c.n;
+    p.eps = c.eps;
+    p.quant_mode = c.quant;
+    if (fn(p, pl.grid, (hipStream_t)stream) != hipSuccess) return ARF_ERR_HIP;
+    return ARF_OK;
+}
+
+// ---- utility kernels -----------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void e4m3_encode_kernel(const float* __restrict__ in,
+                                                          uint8_t* __restrict__ out,
+                                                          int64_t n) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = i + k < n ? in[i + k] : 0.0f;
+    const uint32_t w = arf::e4m3x4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (i + k < n) out[i + k] = (uint8_t)(w >> (8 * k));
+}
+
+// Contiguous spans of 256 lanes x 8 x 16 bytes per workgroup iteration, through a buffer
+// resource per span (the fused kernel's load/store forms, non-temporal).
+constexpr int kCopyUnroll = 8;
+constexpr int64_t kCopySpan = 256 * kCopyUnroll * 16;
+
+__global__ __launch_bounds__(256) void stream_copy_kernel(char* __restrict__ dst,
+                                                          const char* __restrict__ src,
+                                                          int64_t bytes) {
+    for (int64_t s = (int64_t)blockIdx.x * kCopySpan; s < bytes;
+         s += (int64_t)gridDim.x * kCopySpan) {
+        const int64_t left = bytes - s;
+        const uint32_t n = (uint32_t)(left < kCopySpan ? left : kCopySpan);
+        const auto rs = arf::make_rsrc(src + s, n);
+        const auto rd = arf::make_rsrc(dst + s, n);
+        arf::u32x4 v[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u)
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(
+                rs, (uint32_t)(u * 256 + threadIdx.x) * 16u, 0, arf::kAuxStream);
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                v[u], rd, (uint32_t)(u * 256 + threadIdx.x) * 16u, 0, arf::kAuxStream);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+arf_status arf_reduce_add_rmsnorm(const void* partials, int32_t n_shards, int64_t tokens,
+                                  int32_t hidden, int32_t partial_dtype, int32_t act_dtype,
+                                  const void* residual_in, void* residual_out,
+                                  const void* gamma, float eps, void* norm_out,
+                                  void* stream) {
+    Call c{partials, n_shards, tokens, hidden, partial_dtype, act_dtype, residual_in,
+           residual_out, gamma, eps, norm_out, nullptr, arf::kQuantNone, nullptr, nullptr};
+    return run(c, stream);
+}
+
+arf_status arf_reduce_add_rmsnorm_quant(const void* partials, int32_t n_shards,
+                                        int64_t tokens, int32_t hidden,
+                                        int32_t partial_dtype, int32_t act_dtype,
+                                        const void* residual_in, void* residual_out,
+                                        const void* gamma, float eps, void* norm_out,
+                                        uint8_t* quant_out, int32_t mode,
+                                        const float* scale_in, float* scale_out,
+                                        void* stream) {
+    int32_t q;
+    if (mode == ARF_QUANT_PER_TENSOR) q = arf::kQuantTensor;
+    else if (mode == ARF_QUANT_PER_TOKEN) q = arf::kQuantToken;
+    else return ARF_ERR_VALUE;
+    Call c{partials, n_shards, tokens, hidden, partial_dtype, act_dtype, residual_in,
+           residual_out, gamma, eps, norm_out, quant_out, q,
+           q == arf::kQuantTensor ? scale_in : nullptr,
+           q == arf::kQuantToken ? scale_out : nullptr};
+    return run(c, stream);
+}
+
+const char* arf_status_string(int32_t s) {
+    switch (s) {
+        case ARF_OK: return "ARF_OK";
+        case ARF_ERR_NULL: return "ARF_ERR_NULL: a required pointer is NULL";
+        case ARF_ERR_SHAPE: return "ARF_ERR_SHAPE: n_shards, tokens or hidden out of range";
+        case ARF_ERR_DTYPE: return "ARF_ERR_DTYPE: unsupported element type combination";
+        case ARF_ERR_ALIGN: return "ARF_ERR_ALIGN: misaligned pointer";
+        case ARF_ERR_ALIAS: return "ARF_ERR_ALIAS: an output overlaps another buffer";
+        case ARF_ERR_NO_OUTPUT: return "ARF_ERR_NO_OUTPUT: no output requested";
+        case ARF_ERR_VALUE: return "ARF_ERR_VALUE: bad eps, mode or geometry override";
+        case ARF_ERR_HIP: return "ARF_ERR_HIP: no usable device or launch failure";
+        default: return "unknown arf_status";
+    }
+}
+
+int32_t arf_version(void) { return ARF_VERSION; }
+
+arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
+                        int32_t partial_dtype, int32_t num_cus, int32_t* out) {
+    if (!out) return ARF_ERR_NULL;
+    if (n_shards < 1 || n_shards > ARF_MAX_SHARDS || tokens < 0 || tokens > INT32_MAX ||
+        hidden <= 0 || hidden % 8 != 0 || hidden > ARF_MAX_HIDDEN)
+        return ARF_ERR_SHAPE;
+    if (partial_dtype != ARF_BF16 && partial_dtype != ARF_F16 && partial_dtype != ARF_F32)
+        return ARF_ERR_DTYPE;
+    if (num_cus <= 0) {
+        arf_status st = device_cus(&num_cus);
+        if (st != ARF_OK) return st;
+    }
+    Plan pl;
+    arf_status st = make_plan(tokens, hidden, num_cus, &pl);
+    if (st != ARF_OK) return st;
+    out[0] = pl.path;
+    out[1] = pl.waves;
+    out[2] = pl.chunks;
+    out[3] = (int32_t)pl.grid;
+    return ARF_OK;
+}
+
+arf_status arf_set_path_override(int32_t path, int32_t waves_per_block,
+                                 int32_t chunks_per_lane) {
+    if (path < 0 || path > 2) return ARF_ERR_VALUE;
+    if (path == 0 && (waves_per_block || chunks_per_lane)) return ARF_ERR_VALUE;
+    if (path == 1 && waves_per_block && waves_per_block != 4) return ARF_ERR_VALUE;
+    if (path == 2 && waves_per_block && !in_menu_w(waves_per_block)) return ARF_ERR_VALUE;
+    if (chunks_per_lane && !in_menu_c(chunks_per_lane)) return ARF_ERR_VALUE;
+    g_path.store(path);
+    g_waves.store(path == 2 ? waves_per_block : 0);
+    g_chunks.store(chunks_per_lane);
+    return ARF_OK;
+}
+
+arf_status arf_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream) {
+    if (n < 0) return ARF_ERR_SHAPE;
+    if (n == 0) return ARF_OK;
+    if (!in || !out) return ARF_ERR_NULL;
+    if (!aligned(in, 4)) return ARF_ERR_ALIGN;
+    if (overlap(span(in, n * 4), span(out, n))) return ARF_ERR_ALIAS;
+    const int64_t blocks = (n + 1023) / 1024;
+    if (blocks > INT32_MAX) return ARF_ERR_SHAPE;
+    void* args[] = {&in, &out, &n};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&e4m3_encode_kernel),
+                           dim3((uint32_t)blocks), dim3(256), args, 0,
+                           (hipStream_t)stream) == hipSuccess
+               ? ARF_OK
+               : ARF_ERR_HIP;
+}
+
+arf_status arf_stream_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+    if (bytes < 0 || bytes % 16 != 0) return ARF_ERR_SHAPE;
+    if (bytes == 0) return ARF_OK;
+    if (!dst || !src) return ARF_ERR_NULL;
+    if (!aligned(dst, 16) || !aligned(src, 16)) return ARF_ERR_ALIGN;
+    if (overlap(span(dst, bytes), span(src, bytes))) return ARF_ERR_ALIAS;
+    int cus = 0;
+    arf_status st = device_cus(&cus);
+    if (st != ARF_OK) return st;
+    const int64_t spans = (bytes + kCopySpan - 1) / kCopySpan;
+    const int64_t cap = (int64_t)cus * 8;
+    const uint32_t grid = (uint32_t)(spans < cap ? spans : cap);
+    char* d = (char*)dst;
+    const char* s = (const char*)src;
+    void* args[] = {&d, &s, &bytes};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&stream_copy_kernel), dim3(grid),
+                           dim3(256), args, 0, (hipStream_t)stream) == hipSuccess
+               ? ARF_OK
+               : ARF_ERR_HIP;
+}
+
+}  // extern "C"

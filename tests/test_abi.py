@@ -1,0 +1,164 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol include/arfuse.h
+declares, and rejects bad arguments before any device call. No kernel is launched:
+every call below fails validation or is empty (tokens == 0), except the no-device case,
+which only runs where no GPU is present."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import shard_reduce_residual_amd as arf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "arfuse.h")
+
+# fake, well-aligned, non-overlapping device addresses: never dereferenced, because
+# every call using them fails validation first
+P, R, RO, G, NO, Q, S = (0x10000000 * k for k in range(1, 8))
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(arf_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = arf.lib()
+    names = declared_symbols()
+    assert len(names) == 8
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(arf.SIGNATURES)
+
+
+def test_version_and_status_strings():
+    assert arf.arf_version() == 100
+    for code, name in enumerate(arf.STATUS):
+        assert arf.arf_status_string(code).startswith(name)
+    assert "unknown" in arf.arf_status_string(99)
+
+
+def call(**kw):
+    a = dict(partials=P, n=2, tokens=4, hidden=64, pdt=0, adt=0, rin=R, rout=RO, gamma=G,
+             eps=1e-6, nout=NO)
+    a.update(kw)
+    return arf.lib().arf_reduce_add_rmsnorm(a["partials"], a["n"], a["tokens"], a["hidden"],
+                                            a["pdt"], a["adt"], a["rin"], a["rout"],
+                                            a["gamma"], a["eps"], a["nout"], None)
+
+
+def callq(**kw):
+    a = dict(partials=P, n=2, tokens=4, hidden=64, pdt=0, adt=0, rin=R, rout=RO, gamma=G,
+             eps=1e-6, nout=NO, q=Q, mode=1, sin=None, sout=S)
+    a.update(kw)
+    return arf.lib().arf_reduce_add_rmsnorm_quant(
+        a["partials"], a["n"], a["tokens"], a["hidden"], a["pdt"], a["adt"], a["rin"],
+        a["rout"], a["gamma"], a["eps"], a["nout"], a["q"], a["mode"], a["sin"], a["sout"],
+        None)
+
+
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, NOOUT, VALUE, HIP = range(9)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(partials=None), NULL), (dict(rin=None), NULL), (dict(gamma=None), NULL),
+    (dict(rout=None, nout=None), NOOUT),
+    (dict(n=0), SHAPE), (dict(n=17), SHAPE), (dict(tokens=-1), SHAPE),
+    (dict(tokens=2 ** 31), SHAPE), (dict(hidden=0), SHAPE), (dict(hidden=12), SHAPE),
+    (dict(hidden=65544), SHAPE),
+    (dict(adt=2), DTYPE), (dict(adt=3), DTYPE), (dict(pdt=1, adt=0), DTYPE),
+    (dict(pdt=0, adt=1), DTYPE),
+    (dict(eps=-1e-6), VALUE), (dict(eps=float("inf")), VALUE), (dict(eps=float("nan")), VALUE),
+    (dict(partials=P + 8), ALIGN), (dict(rout=RO + 2), ALIGN), (dict(gamma=G + 4), ALIGN),
+    (dict(nout=R), ALIAS), (dict(rout=P), ALIAS), (dict(nout=RO), ALIAS),
+    (dict(rout=R + 16), ALIAS), (dict(nout=G), ALIAS),
+    (dict(tokens=0), OK), (dict(tokens=0, rout=R), OK),
+])
+def test_validation(kw, want):
+    assert call(**kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), NULL), (dict(mode=1, sout=None), NULL), (dict(mode=0, sin=None), NULL),
+    (dict(mode=2), VALUE), (dict(mode=-1), VALUE),
+    (dict(sout=S + 2), ALIGN), (dict(q=Q + 8), ALIGN),
+    (dict(q=NO), ALIAS), (dict(sout=Q), ALIAS), (dict(mode=0, sin=RO, sout=None), ALIAS),
+    (dict(rout=None, nout=None, tokens=0), OK),
+    (dict(mode=0, sin=S, sout=None, tokens=0), OK),
+])
+def test_quant_validation(kw, want):
+    assert callq(**kw) == want
+
+
+def test_in_place_residual_passes_validation_and_empty_call_is_ok():
+    # residual_out == residual_in is the one allowed overlap
+    assert call(rout=R, tokens=0) == OK
+
+
+def test_utility_entry_point_validation():
+    L = arf.lib()
+    assert L.arf_e4m3_encode(P, Q, 0, None) == OK
+    assert L.arf_e4m3_encode(None, Q, 8, None) == NULL
+    assert L.arf_e4m3_encode(P, Q, -1, None) == SHAPE
+    assert L.arf_e4m3_encode(P + 2, Q, 8, None) == ALIGN
+    assert L.arf_e4m3_encode(P, P + 4, 8, None) == ALIAS
+    assert L.arf_stream_copy(Q, P, 0, None) == OK
+    assert L.arf_stream_copy(Q, P, 24, None) == SHAPE
+    assert L.arf_stream_copy(Q, None, 32, None) == NULL
+    assert L.arf_stream_copy(Q + 8, P, 32, None) == ALIGN
+    assert L.arf_stream_copy(P + 16, P, 64, None) == ALIAS
+
+
+def plan(n, t, h, pd=0, cus=256):
+    return arf.arf_get_plan(n, t, h, pd, cus)
+
+
+def test_plan_covers_the_row_and_follows_the_menu():
+    try:
+        for h in (8, 64, 264, 1024, 2048, 4096, 7168, 8192, 16384, 32768, 65536):
+            for t in (1, 16, 128, 2048, 8192):
+                p = plan(8, t, h)
+                lanes = 64 if p["path"] == 1 else 64 * p["waves"]
+                assert lanes * p["chunks"] * 8 >= h
+                assert p["chunks"] in (1, 2, 4, 8)
+                if p["path"] == 1:
+                    assert p["waves"] == 4 and p["grid"] == (t + 3) // 4
+                else:
+                    assert p["waves"] in (2, 4, 8, 16) and p["grid"] == t
+    finally:
+        arf.arf_set_path_override(0)
+
+
+def test_plan_for_the_named_workloads():
+    assert plan(8, 8192, 16384) == {"path": 2, "waves": 4, "chunks": 8, "grid": 8192}
+    assert plan(4, 2048, 7168, 2) == {"path": 2, "waves": 4, "chunks": 4, "grid": 2048}
+    assert plan(8, 128, 4096)["chunks"] == 1
+    assert plan(2, 16, 1024)["path"] == 2
+
+
+def test_path_override_forces_and_rejects():
+    try:
+        arf.arf_set_path_override(1)
+        assert plan(8, 8192, 1024)["path"] == 1
+        with pytest.raises(arf.ArfError):
+            plan(8, 8, 8192)             # a wavefront cannot cover 8192 with 8 chunks/lane
+        arf.arf_set_path_override(2, 16, 1)
+        assert plan(8, 8, 8192) == {"path": 2, "waves": 16, "chunks": 1, "grid": 8}
+        with pytest.raises(arf.ArfError):
+            plan(8, 8, 16384)
+        for bad in ((3, 0, 0), (0, 4, 0), (2, 3, 0), (2, 4, 3), (1, 8, 0)):
+            with pytest.raises(arf.ArfError):
+                arf.arf_set_path_override(*bad)
+    finally:
+        arf.arf_set_path_override(0)
+    assert plan(8, 8192, 16384)["waves"] == 4
+
+
+def test_no_device_returns_hip_error():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this case would launch on fake addresses")
+    assert call() == HIP
+    assert arf.lib().arf_stream_copy(Q, P, 64, None) == HIP

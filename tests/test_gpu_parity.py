@@ -1,0 +1,360 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle, element by element.
+
+Tolerances (fixed here, per output):
+  residual_out  bit-exact;
+  norm_out      at most 1 ulp of the activation type (ordinal distance, +0 == -0);
+  fp8 codes     at most 1 code (ordinal distance);
+  scale_out     relative difference at most 2^-7.
+Every element must pass. Output buffers are poisoned (0xFF) and followed by canary
+bytes, so an element that is never written, or a write past the end, fails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import shard_reduce_residual_amd as arf
+import workloads
+from helpers import code_diff8, e4m3_brute, ulp_diff16
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+GUARD = 512
+POISON, CANARY = 0xFF, 0x5A
+TORCH = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+THREADS = min(16, oracle.default_threads())
+
+
+def say(msg):
+    print("[case] " + msg, flush=True)
+
+
+class Out:
+    """An output tensor with a poisoned body and a canary tail."""
+
+    def __init__(self, shape, dtype):
+        n = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+        self.nbytes = n
+        self.raw = torch.full((n + GUARD,), POISON, dtype=torch.uint8, device=DEV)
+        self.raw[n:] = CANARY
+        self.t = self.raw[:n].view(dtype).view(shape)
+
+    def canary_ok(self):
+        return bool((self.raw[self.nbytes:] == CANARY).all().item())
+
+
+def run_gpu(p, r, g, eps, act, *, res=True, norm=True, quant=None, scale=None,
+            in_place=False):
+    """p, r, g: device tensors. Returns host numpy results (uint16 bits / uint8 / f32)."""
+    t, h = r.shape
+    adt = TORCH[act]
+    rin = r.clone() if in_place else r
+    rout = None
+    if in_place:
+        rout_t = rin
+    elif res:
+        rout = Out((t, h), adt)
+        rout_t = rout.t
+    else:
+        rout_t = None
+    nout = Out((t, h), adt) if norm else None
+    out = {}
+    if quant is None:
+        arf.arf_reduce_add_rmsnorm(p, rin, g, eps, residual_out=rout_t,
+                                   norm_out=nout.t if nout else None)
+    else:
+        q = Out((t, h), torch.uint8)
+        sin = sout = None
+        if quant == "per_tensor":
+            sin = torch.tensor([scale], dtype=torch.float32, device=DEV)
+            mode = arf.ARF_QUANT_PER_TENSOR
+        else:
+            sout = Out((t,), torch.float32)
+            mode = arf.ARF_QUANT_PER_TOKEN
+        arf.arf_reduce_add_rmsnorm_quant(p, rin, g, eps, q.t, mode, scale_in=sin,
+                                         scale_out=sout.t if sout else None,
+                                         residual_out=rout_t,
+                                         norm_out=nout.t if nout else None)
+        torch.cuda.synchronize()
+        assert q.canary_ok()
+        out["quant_out"] = q.t.cpu().numpy()
+        if sout is not None:
+            assert sout.canary_ok()
+            out["scale_out"] = sout.t.cpu().numpy()
+    torch.cuda.synchronize()
+    if rout_t is not None:
+        if rout is not None:
+            assert rout.canary_ok()
+        out["residual_out"] = workloads.to_bits(rout_t)
+    if nout is not None:
+        assert nout.canary_ok()
+        out["norm_out"] = workloads.to_bits(nout.t)
+    return out
+
+
+def run_oracle(p, r, g, eps, pd, act, **kw):
+    return oracle.reduce_add_rmsnorm(workloads.to_bits(p), workloads.to_bits(r),
+                                     workloads.to_bits(g), eps, partial_dtype=pd,
+                                     act_dtype=act, n_threads=THREADS, **kw)
+
+
+def compare(gpu, ref, label="", min_exact=0.999):
+    stats = {}
+    if "residual_out" in ref and "residual_out" in gpu:
+        bad = np.nonzero(gpu["residual_out"] != ref["residual_out"])
+        assert bad[0].size == 0, "%s residual_out differs at %s" % (label, list(zip(*bad))[:5])
+    if "norm_out" in ref and "norm_out" in gpu:
+        d = ulp_diff16(gpu["norm_out"], ref["norm_out"])
+        stats["norm_exact"] = float((d == 0).mean())
+        assert d.max() <= 1, "%s norm_out differs by %d ulp" % (label, d.max())
+        assert stats["norm_exact"] >= min_exact, (label, stats)
+    if "quant_out" in ref:
+        d = code_diff8(gpu["quant_out"], ref["quant_out"])
+        stats["fp8_exact"] = float((d == 0).mean())
+        assert d.max() <= 1, "%s fp8 codes differ by %d" % (label, d.max())
+    if "scale_out" in ref:
+        rel = np.abs(gpu["scale_out"].astype(np.float64) / ref["scale_out"] - 1.0)
+        rel = np.where(ref["scale_out"] == 0, np.abs(gpu["scale_out"]), rel)
+        assert rel.max() <= 2.0 ** -7, (label, rel.max())
+    return stats
+
+
+def upload(w):
+    p, r, g = workloads.generate(w, "cpu")
+    return (p, r, g), (p.to(DEV), r.to(DEV), g.to(DEV))
+
+
+# ---- the five workloads --------------------------------------------------------------------
+
+@pytest.mark.parametrize("key", ["c0", "c1", "c2", "c3"])
+def test_workload_parity_full(key):
+    w = workloads.WORKLOADS[key]
+    say("workload %s full compare" % w.name)
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    scale = None
+    if w.quant == "per_tensor":
+        # the per-tensor scale is max|y| / 448 of the oracle's own normalised output
+        y = oracle.act_to_f32(run_oracle(p, r, g, w.eps, w.partial_dtype, w.act_dtype)["norm_out"],
+                              w.act_dtype)
+        scale = float(np.float32(np.abs(y).max()) / np.float32(448.0))
+    ref = run_oracle(p, r, g, w.eps, w.partial_dtype, w.act_dtype, quant=w.quant,
+                     scale_in=scale)
+    got = run_gpu(pd_, rd, gd, w.eps, w.act_dtype, quant=w.quant, scale=scale)
+    stats = compare(got, ref, w.name)
+    print(w.name, stats)
+
+
+def test_workload_c4_full_size_sampled_rows():
+    w = workloads.WORKLOADS["c4"]
+    say("workload %s full size, sampled rows" % w.name)
+    p, r, g = workloads.generate(w, DEV)
+    t, h = w.tokens, w.hidden
+    rout = torch.empty((t, h), dtype=torch.bfloat16, device=DEV)
+    nout = torch.empty((t, h), dtype=torch.bfloat16, device=DEV)
+    q = torch.empty((t, h), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((t,), dtype=torch.float32, device=DEV)
+    arf.arf_reduce_add_rmsnorm_quant(p, r, g, w.eps, q, arf.ARF_QUANT_PER_TOKEN, scale_out=sc,
+                                     residual_out=rout, norm_out=nout)
+    torch.cuda.synchronize()
+    rows = sorted(set([0, 1, 2, t // 2, t - 2, t - 1] +
+                      list(np.random.default_rng(4).choice(t, 40, replace=False))))
+    idx = torch.tensor(rows, device=DEV)
+    ref = run_oracle(p[:, idx].contiguous(), r[idx].contiguous(), g, w.eps, "bf16", "bf16",
+                     quant="per_token")
+    got = {"residual_out": workloads.to_bits(rout[idx]), "norm_out": workloads.to_bits(nout[idx]),
+           "quant_out": q[idx].cpu().numpy(), "scale_out": sc[idx].cpu().numpy()}
+    print(compare(got, ref, w.name))
+    # properties over every row: the scale is max|y|/448 of the row, and the element(s)
+    # of largest magnitude carry the code 448
+    y = nout.float().abs()
+    amax = y.amax(dim=1)
+    assert torch.allclose(sc.double() * 448.0, amax.double(), rtol=2.0 ** -22, atol=0)
+    top = (y == amax[:, None])
+    assert bool(((q[top] & 0x7F) == 0x7E).all())
+    del p, r, rout, nout, q
+
+
+# ---- sizes, shapes, types and paths --------------------------------------------------------
+
+def _case(n, t, h, pd, ad, seed, quant=None, eps=1e-6, std=1.0):
+    w = workloads.Workload("sweep", n, t, h, pd, ad, std, 1.0, eps, quant, seed)
+    return w
+
+
+SWEEP = [  # (n, t, h)
+    (1, 3, 8), (2, 5, 16), (3, 17, 64), (16, 2, 264), (7, 9, 1024), (8, 33, 2048),
+    (5, 4, 4096), (4, 6, 7168), (8, 3, 8192), (9, 2, 16384), (2, 1, 32768), (1, 2, 65536),
+    (16, 2, 65536), (12, 3, 7176), (6, 65, 520),
+]
+
+
+@pytest.mark.parametrize("pd,ad", [("bf16", "bf16"), ("f16", "f16"), ("f32", "bf16"),
+                                   ("f32", "f16")])
+def test_sweep_shapes_auto_path(pd, ad):
+    for i, (n, t, h) in enumerate(SWEEP):
+        w = _case(n, t, h, pd, ad, 100 + i, quant="per_token" if i % 2 else None)
+        say("sweep auto n=%d t=%d h=%d %s/%s quant=%s" % (n, t, h, pd, ad, w.quant))
+        (p, r, g), (pd_, rd, gd) = upload(w)
+        ref = run_oracle(p, r, g, w.eps, pd, ad, quant=w.quant)
+        got = run_gpu(pd_, rd, gd, w.eps, ad, quant=w.quant)
+        compare(got, ref, "n=%d t=%d h=%d" % (n, t, h), min_exact=0.99)
+
+
+def _geometries(h):
+    hc = h // 8
+    out = []
+    for c in (1, 2, 4, 8):
+        if 64 * c >= hc:
+            out.append((1, 4, c))
+        for wv in (2, 4, 8, 16):
+            if wv * 64 * c >= hc:
+                out.append((2, wv, c))
+    return out
+
+
+@pytest.mark.parametrize("h", [264, 1024, 4096, 7168])
+def test_every_geometry_matches_the_oracle(h):
+    w = _case(8, 7, h, "bf16", "bf16", 7 + h, quant="per_token")
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    ref = run_oracle(p, r, g, w.eps, "bf16", "bf16", quant="per_token")
+    try:
+        for path, wv, c in _geometries(h):
+            say("geometry h=%d path=%d waves=%d chunks=%d" % (h, path, wv, c))
+            arf.arf_set_path_override(path, wv if path == 2 else 0, c)
+            got = run_gpu(pd_, rd, gd, w.eps, "bf16", quant="per_token")
+            compare(got, ref, "h=%d path=%d w=%d c=%d" % (h, path, wv, c), min_exact=0.99)
+    finally:
+        arf.arf_set_path_override(0)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16])
+def test_every_shard_count(n):
+    w = _case(n, 4, 2048, "bf16", "bf16", 300 + n)
+    say("shards n=%d" % n)
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    compare(run_gpu(pd_, rd, gd, w.eps, "bf16"), run_oracle(p, r, g, w.eps, "bf16", "bf16"))
+
+
+def test_output_subsets_and_in_place():
+    w = _case(4, 9, 4096, "bf16", "bf16", 11)
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    full = run_oracle(p, r, g, w.eps, "bf16", "bf16", quant="per_token")
+    for kw in (dict(res=True, norm=False), dict(res=False, norm=True),
+               dict(in_place=True), dict(res=False, norm=False, quant="per_token"),
+               dict(in_place=True, norm=False, quant="per_token")):
+        say("subset %s" % kw)
+        got = run_gpu(pd_, rd, gd, w.eps, "bf16", **kw)
+        ref = {k: v for k, v in full.items() if k in got}
+        if "quant_out" not in got:
+            ref.pop("scale_out", None)
+        compare(got, ref, str(kw))
+    # in place really overwrote the residual, and the input partials are untouched
+    rin = rd.clone()
+    arf.arf_reduce_add_rmsnorm(pd_, rin, gd, w.eps, residual_out=rin)
+    torch.cuda.synchronize()
+    assert np.array_equal(workloads.to_bits(rin), full["residual_out"])
+    assert torch.equal(pd_.cpu(), p)
+
+
+def test_per_tensor_scales_and_zero_rows():
+    w = _case(2, 6, 1024, "bf16", "bf16", 12, quant="per_tensor")
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    for scale in (2.0 ** -3, 0.0123, 1.0, 0.0, -1.0):
+        say("per-tensor scale %g" % scale)
+        ref = run_oracle(p, r, g, w.eps, "bf16", "bf16", quant="per_tensor", scale_in=scale)
+        compare(run_gpu(pd_, rd, gd, w.eps, "bf16", quant="per_tensor", scale=scale), ref)
+    say("all-zero rows, per-token")
+    z = torch.zeros_like(pd_)
+    zr = torch.zeros_like(rd)
+    got = run_gpu(z, zr, gd, w.eps, "bf16", quant="per_token")
+    assert np.all(got["quant_out"] == 0) and np.all(got["scale_out"] == 0)
+    assert np.all((got["norm_out"] & 0x7FFF) == 0) and np.all(got["residual_out"] == 0)
+
+
+def test_eps_values_and_outliers():
+    for eps in (0.0, 1e-6, 0.5):
+        w = workloads.Workload("out", 4, 5, 7168, "f32", "bf16", 1.0, 1.0, eps, None, 21,
+                               outlier_frac=0.01, outlier_scale=100.0)
+        say("fp32 partials with outliers eps=%g" % eps)
+        (p, r, g), (pd_, rd, gd) = upload(w)
+        compare(run_gpu(pd_, rd, gd, eps, "bf16"), run_oracle(p, r, g, eps, "f32", "bf16"))
+
+
+def test_rank_order_vector_on_gpu():
+    # 2^24 + 1 + 1 - 2^24 in rank order is 0 (a pairwise tree gives 1, the exact sum 2)
+    say("rank-order vector")
+    h = 64
+    vals = torch.tensor([2.0 ** 24, 1.0, 1.0, -2.0 ** 24])
+    p = vals[:, None, None].expand(4, 3, h).contiguous().to(torch.bfloat16).to(DEV)
+    r = torch.full((3, h), 0.5, dtype=torch.bfloat16, device=DEV)
+    g = torch.ones((h,), dtype=torch.bfloat16, device=DEV)
+    got = run_gpu(p, r, g, 1e-6, "bf16")
+    assert np.all(got["residual_out"] == 0x3F00)   # 0.5
+
+
+def test_empty_call_writes_nothing():
+    say("tokens == 0")
+    p = torch.empty((2, 0, 64), dtype=torch.bfloat16, device=DEV)
+    r = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    g = torch.ones((64,), dtype=torch.bfloat16, device=DEV)
+    o = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    arf.arf_reduce_add_rmsnorm(p, r, g, 1e-6, residual_out=o, norm_out=None)
+    torch.cuda.synchronize()
+
+
+def test_repeat_runs_are_bit_identical():
+    w = workloads.WORKLOADS["c1"]
+    say("determinism %s" % w.name)
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    a = run_gpu(pd_, rd, gd, w.eps, "bf16", quant="per_token")
+    b = run_gpu(pd_, rd, gd, w.eps, "bf16", quant="per_token")
+    for k in a:
+        assert np.array_equal(a[k], b[k])
+
+
+# ---- the quantiser's conversion and the copy probe -----------------------------------------
+
+def test_e4m3_conversion_matches_the_oracle():
+    say("e4m3 encoder")
+    from helpers import e4m3_values
+    vals = e4m3_values()
+    mids = (vals[:-1] + vals[1:]) / 2
+    pts = np.concatenate([vals, mids, [456.0, 464.0, 472.0, 480.0, 1e4]]).astype(np.float32)
+    pts = np.concatenate([pts, np.nextafter(pts, np.float32(0)), np.nextafter(pts, np.float32(np.inf))])
+    rng = np.random.default_rng(3)
+    pts = np.concatenate([pts, np.exp2(rng.uniform(-16, 12, 1 << 20)).astype(np.float32)])
+    pts = np.concatenate([pts, -pts, rng.integers(0, 2 ** 32, 1 << 20, dtype=np.uint64)
+                          .astype(np.uint32).view(np.float32),
+                          np.array([np.inf, -np.inf, 0.0, -0.0, np.nan], np.float32)])
+    x = torch.from_numpy(pts).to(DEV)
+    out = torch.empty(x.numel(), dtype=torch.uint8, device=DEV)
+    arf.arf_e4m3_encode(x, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = oracle.f32_to_e4m3(pts)
+    nan = np.isnan(pts)
+    bad = np.nonzero(got[~nan] != want[~nan])[0]
+    assert bad.size == 0, [(float(pts[~nan][i]), hex(got[~nan][i]), hex(want[~nan][i]))
+                           for i in bad[:10]]
+    assert np.all((got[nan] & 0x7F) == 0x7F)
+    # odd length: the tail is converted and nothing past it is written
+    y = torch.from_numpy(pts[:1001]).to(DEV)
+    o2 = torch.full((1001 + 64,), 0x5A, dtype=torch.uint8, device=DEV)
+    arf.arf_e4m3_encode(y, o2[:1001])
+    torch.cuda.synchronize()
+    o2 = o2.cpu().numpy()
+    assert np.array_equal(o2[:1001][~nan[:1001]], want[:1001][~nan[:1001]])
+    assert np.all(o2[1001:] == 0x5A)
+    assert np.array_equal(e4m3_brute(pts[:4096]), want[:4096])
+
+
+def test_stream_copy_is_exact():
+    for nbytes in (16, 4096 + 48, 3 * 32768 + 16, 64 << 20):
+        say("stream copy %d bytes" % nbytes)
+        src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=DEV)
+        dst = torch.full((nbytes + GUARD,), CANARY, dtype=torch.uint8, device=DEV)
+        arf.arf_stream_copy(dst, src, nbytes)
+        torch.cuda.synchronize()
+        assert torch.equal(dst[:nbytes], src)
+        assert bool((dst[nbytes:] == CANARY).all())
