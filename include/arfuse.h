@@ -133,7 +133,7 @@ arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
  * TEST AND TUNING ONLY; process-wide, not to be changed while other threads call the
  * library. path 0 = automatic (the other two arguments must be 0); 1 = one row per
  * wavefront; 2 = one row per workgroup. waves_per_block (1 row per workgroup only:
- * 2, 4, 8 or 16) and chunks_per_lane (1, 2, 4 or 8) force the geometry when non-zero.
+ * 4, 8 or 16) and chunks_per_lane (1, 2, 4 or 8) force the geometry when non-zero.
  * A forced geometry that cannot cover a call's hidden size makes that call return
  * ARF_ERR_VALUE. Returns ARF_ERR_VALUE for values outside these sets.
  */

@@ -144,9 +144,15 @@ __device__ __forceinline__ float wave_max(float v) {
 // ---- the fused kernel -------------------------------------------------------------------
 //
 // PT: partial element type tag (ActBF16 / ActF16 / PartF32); AT: activation tag.
-// NMAX: compile-time upper bound of n_shards (shards r >= n_shards are skipped by a
-// uniform branch). C: chunks per lane. WAVES: wavefronts per workgroup. ROW_PER_WAVE:
-// each wavefront owns one row (else the whole workgroup owns one row).
+// N: number of shards (exact). C: chunks per lane. WAVES: wavefronts per workgroup.
+// ROW_PER_WAVE: each wavefront owns one row (else the whole workgroup owns one row).
+// DEPTH: shards in flight while one is added.
+//
+// The row is streamed shard by shard ("shard-major"): the lanes of the row read shard r's
+// whole row (C chunks each), add it into fp32 accumulators in rank order, and meanwhile the
+// loads of the next DEPTH-1 shards are in flight; the residual row follows the last shard.
+// At any moment a row therefore touches one or two long sequential streams instead of N+1
+// interleaved ones, which measured a few per cent faster in HBM than chunk-by-chunk order.
 template <class PT> struct PartTraits {
     static constexpr int kPieces = 1;   // 16-byte loads per chunk per shard
     static constexpr int kBytes = 2;
@@ -169,8 +175,9 @@ __device__ __forceinline__ void load_partial_chunk(AT, u32x4 const (&v)[2], floa
     }
 }
 
-template <class PT, class AT, int NMAX, int C, int WAVES, bool ROW_PER_WAVE>
+template <class PT, class AT, int N, int C, int WAVES, bool ROW_PER_WAVE, int DEPTH = 2>
 __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p) {
+    static_assert(N >= 1 && C >= 1 && DEPTH >= 2, "bad instantiation");
     constexpr int PW = PartTraits<PT>::kPieces;
     constexpr int G = ROW_PER_WAVE ? 64 : WAVES * 64;   // lanes per row
     const int lane = threadIdx.x & 63;
@@ -188,7 +195,6 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
     }
 
     const uint32_t H = (uint32_t)p.hidden;
-    const int n = p.n_shards;
     const uint32_t act_row = H * 2u;
     const uint32_t part_row = H * (uint32_t)PartTraits<PT>::kBytes;
     const int64_t act_off = row * (int64_t)act_row;
@@ -198,51 +204,62 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
     const auto y_out = make_rsrc((char*)p.norm_out + act_off, p.norm_out ? act_row : 0u);
     const auto g_in = make_rsrc(p.gamma, act_row);
 
-    __amdgpu_buffer_rsrc_t part[NMAX];
+    __amdgpu_buffer_rsrc_t part[N];
 #pragma unroll
-    for (int r = 0; r < NMAX; ++r)
+    for (int r = 0; r < N; ++r)
         part[r] = make_rsrc((const char*)p.partials +
                                 ((int64_t)r * p.tokens + row) * (int64_t)part_row,
                             part_row);
 
-    // ---- pass over HBM: rank-order sum, cast, residual add, cast, store, sum of squares
+    // ---- pass over HBM: rank-order fp32 sum of the shards
+    u32x4 buf[DEPTH][C][PW];
+    u32x4 rv[C];
+    float acc[C][8];
+    auto issue_shard = [&](int r, int slot) {
+#pragma unroll
+        for (int j = 0; j < C; ++j)
+#pragma unroll
+            for (int w = 0; w < PW; ++w)
+                buf[slot][j][w] = __builtin_amdgcn_raw_buffer_load_b128(
+                    part[r], (uint32_t)(j * G + gl) * (16u * PW) + 16u * w, 0, kAuxStream);
+    };
+    auto issue_residual = [&]() {
+#pragma unroll
+        for (int j = 0; j < C; ++j)
+            rv[j] = __builtin_amdgcn_raw_buffer_load_b128(r_in, (uint32_t)(j * G + gl) * 16u, 0,
+                                                          kAuxStream);
+    };
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d)
+        if (d < N) issue_shard(d, d);
+    if (N < DEPTH - 1) issue_residual();
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+        if (r + DEPTH - 1 < N) issue_shard(r + DEPTH - 1, (r + DEPTH - 1) % DEPTH);
+        else if (r + DEPTH - 1 == N) issue_residual();
+        const int slot = r % DEPTH;
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            float t[8];
+            load_partial_chunk(AT{}, buf[slot][j], t);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[j][e] = r == 0 ? t[e] : acc[j][e] + t[e];
+        }
+    }
+
+    // ---- cast, residual add, cast, store; sum of squares of the stored value
     double ss = 0.0;
     u32x4 xr[C];
 #pragma unroll
     for (int j = 0; j < C; ++j) {
-        const uint32_t chunk = (uint32_t)(j * G + gl);
-        const uint32_t off_a = chunk * 16u;
-        const uint32_t off_p = chunk * 16u * PW;
-        u32x4 pv[NMAX][PW];
-#pragma unroll
-        for (int r = 0; r < NMAX; ++r) {
-            if (r < n) {
-#pragma unroll
-                for (int w = 0; w < PW; ++w)
-                    pv[r][w] = __builtin_amdgcn_raw_buffer_load_b128(part[r], off_p + 16u * w,
-                                                                     0, kAuxStream);
-            }
-        }
-        const u32x4 rv = __builtin_amdgcn_raw_buffer_load_b128(r_in, off_a, 0, kAuxStream);
-
-        float acc[8];
-        load_partial_chunk(AT{}, pv[0], acc);
-#pragma unroll
-        for (int r = 1; r < NMAX; ++r) {
-            if (r < n) {
-                float t[8];
-                load_partial_chunk(AT{}, pv[r], t);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] = acc[e] + t[e];
-            }
-        }
         float s[8], res[8], sum[8];
-        unpack8(AT{}, pack8(AT{}, acc), s);      // reduced value in the activation type
-        unpack8(AT{}, rv, res);
+        unpack8(AT{}, pack8(AT{}, acc[j]), s);   // reduced value in the activation type
+        unpack8(AT{}, rv[j], res);
 #pragma unroll
         for (int e = 0; e < 8; ++e) sum[e] = s[e] + res[e];
         const u32x4 rr = pack8(AT{}, sum);       // residual_out
-        __builtin_amdgcn_raw_buffer_store_b128(rr, r_out, off_a, 0, kAuxStream);
+        __builtin_amdgcn_raw_buffer_store_b128(rr, r_out, (uint32_t)(j * G + gl) * 16u, 0,
+                                               kAuxStream);
         xr[j] = rr;
         float x[8];
         unpack8(AT{}, rr, x);
@@ -325,12 +342,13 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
 }
 
 // Host-side launcher for one instantiation; returns the launch's own status.
-template <class PT, class AT, int NMAX, int C, int WAVES, bool ROW_PER_WAVE>
+template <class PT, class AT, int N, int C, int WAVES, bool ROW_PER_WAVE, int DEPTH = 2>
 hipError_t launch_fused(const Params& p, uint32_t grid, hipStream_t stream) {
     Params arg = p;
     void* args[] = {&arg};
     return hipLaunchKernel(
-        reinterpret_cast<const void*>(&fused_reduce_add_rmsnorm<PT, AT, NMAX, C, WAVES, ROW_PER_WAVE>),
+        reinterpret_cast<const void*>(
+            &fused_reduce_add_rmsnorm<PT, AT, N, C, WAVES, ROW_PER_WAVE, DEPTH>),
         dim3(grid), dim3(WAVES * 64), args, 0, stream);
 }
 

@@ -27,46 +27,62 @@ struct Plan {
 };
 
 bool in_menu_c(int c) { return c == 1 || c == 2 || c == 4 || c == 8; }
-bool in_menu_w(int w) { return w == 2 || w == 4 || w == 8 || w == 16; }
+bool in_menu_w(int w) { return w == 4 || w == 8 || w == 16; }
 
-// Launch geometry. hidden/8 chunks per row are spread over the lanes that own the row.
-//  * one row per wavefront (4 wavefronts per workgroup) when a wavefront covers the row
-//    with at most 8 chunks per lane and there are enough rows to give every compute unit
-//    several workgroups;
-//  * otherwise one row per workgroup. With many rows (at least 2 per compute unit) each
-//    lane takes several chunks so that a workgroup stays small (about 4 wavefronts) and
-//    several rows share a compute unit; with few rows the row is spread over as many
-//    wavefronts as possible (one chunk per lane) to expose parallelism.
-arf_status make_plan(int64_t tokens, int32_t hidden, int num_cus, Plan* pl) {
+int pow2_at_least(int64_t v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Launch geometry: the hidden/8 chunks of a row are spread over the lanes that own it.
+// Fitted to sweeps on MI355X (256 CUs) over hidden 1024..16384, 16..32768 tokens, 2..8
+// bf16 shards and 4 fp32 shards:
+//  * one row per wavefront for short rows (<= 512 chunks) with a moderate token count
+//    (2 to 8 rows per compute unit);
+//  * otherwise one row per workgroup:
+//    - few rows (< 2 per compute unit): 8 wavefronts per row, so that each row exposes
+//      more parallel loads;
+//    - fp32 partials: 16 wavefronts, one chunk per lane where the row allows;
+//    - otherwise 4 wavefronts with up to 8 chunks per lane, so that several rows share a
+//      compute unit; rows above 2048 chunks use 16 wavefronts.
+arf_status make_plan(int64_t tokens, int32_t hidden, int32_t pdt, int num_cus, Plan* pl) {
     const int hc = hidden / 8;
     int path = g_path.load(), waves = g_waves.load(), chunks = g_chunks.load();
     if (path == 0) {
-        const bool enough_rows = tokens >= 8LL * num_cus;
-        path = (hc <= 64 * 8 && enough_rows) ? 1 : 2;
         waves = chunks = 0;
+        const bool many_rows = tokens >= 2LL * num_cus;
+        if (hc <= 512 && many_rows && tokens <= 8LL * num_cus) {
+            path = 1;
+        } else {
+            path = 2;
+            if (!many_rows) {
+                waves = 8;
+            } else if (pdt == ARF_F32) {
+                waves = 16;
+            } else {
+                waves = 4;
+            }
+            if (hc > waves * 64 * 8) waves = 16;
+            chunks = pow2_at_least(div_up(hc, waves * 64));
+        }
     }
     if (path == 1) {
         waves = 4;
-        if (chunks == 0) {
-            for (chunks = 1; chunks < 8 && 64 * chunks < hc; chunks *= 2) {}
-        }
-        if (64 * chunks < hc) return ARF_ERR_VALUE;
+        if (chunks == 0) chunks = pow2_at_least(div_up(hc, 64));
+        if (chunks > 8 || 64 * chunks < hc) return ARF_ERR_VALUE;
         pl->grid = (uint32_t)((tokens + 3) / 4);
     } else {
-        if (waves && chunks) {
-            // forced
-        } else if (chunks) {
-            for (waves = 2; waves < 16 && waves * 64 * chunks < hc; waves *= 2) {}
-        } else if (waves) {
-            for (chunks = 1; chunks < 8 && waves * 64 * chunks < hc; chunks *= 2) {}
-        } else if (tokens >= 2LL * num_cus) {
-            for (chunks = 1; chunks < 8 && 4 * 64 * chunks < hc; chunks *= 2) {}
-            for (waves = 2; waves < 16 && waves * 64 * chunks < hc; waves *= 2) {}
-        } else {
-            for (chunks = 1; chunks < 8 && 16 * 64 * chunks < hc; chunks *= 2) {}
-            for (waves = 2; waves < 16 && waves * 64 * chunks < hc; waves *= 2) {}
+        if (waves == 0 && chunks == 0) {
+            waves = 4;
+            chunks = pow2_at_least(div_up(hc, waves * 64));
+        } else if (waves == 0) {
+            for (waves = 4; waves < 16 && waves * 64 * chunks < hc; waves *= 2) {}
+        } else if (chunks == 0) {
+            chunks = pow2_at_least(div_up(hc, waves * 64));
         }
-        if (waves * 64 * chunks < hc) return ARF_ERR_VALUE;
+        if (chunks > 8 || waves * 64 * chunks < hc) return ARF_ERR_VALUE;
         pl->grid = (uint32_t)tokens;
     }
     pl->path = path;
@@ -75,16 +91,21 @@ arf_status make_plan(int64_t tokens, int32_t hidden, int num_cus, Plan* pl) {
     return ARF_OK;
 }
 
-int nmax_for(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 8 ? 8 : 16; }
-
-launch_fn lookup(int pdt, int adt, int nmax, const Plan& pl) {
+launch_fn lookup(int pdt, int adt, int n, const Plan& pl) {
     const bool rpw = pl.path == 1;
+    const int w = pl.waves, c = pl.chunks;
+#define ARF_BY_RANGE(PD, AD)                                                   \
+    if (n <= 4) return arf::lookup_##PD##_##AD##_n01_04(n, rpw, w, c);         \
+    if (n <= 8) return arf::lookup_##PD##_##AD##_n05_08(n, rpw, w, c);         \
+    if (n <= 12) return arf::lookup_##PD##_##AD##_n09_12(n, rpw, w, c);        \
+    return arf::lookup_##PD##_##AD##_n13_16(n, rpw, w, c);
     if (adt == ARF_BF16) {
-        return pdt == ARF_F32 ? arf::lookup_f32_bf16(nmax, rpw, pl.waves, pl.chunks)
-                              : arf::lookup_bf16_bf16(nmax, rpw, pl.waves, pl.chunks);
+        if (pdt == ARF_F32) { ARF_BY_RANGE(f32, bf16) }
+        ARF_BY_RANGE(bf16, bf16)
     }
-    return pdt == ARF_F32 ? arf::lookup_f32_f16(nmax, rpw, pl.waves, pl.chunks)
-                          : arf::lookup_f16_f16(nmax, rpw, pl.waves, pl.chunks);
+    if (pdt == ARF_F32) { ARF_BY_RANGE(f32, f16) }
+    ARF_BY_RANGE(f16, f16)
+#undef ARF_BY_RANGE
 }
 
 arf_status device_cus(int* cus) {
@@ -182,8 +203,8 @@ arf_status run(const Call& c, void* stream) {
     int cus = 0;
     if ((st = device_cus(&cus)) != ARF_OK) return st;
     Plan pl;
-    if ((st = make_plan(c.tokens, c.hidden, cus, &pl)) != ARF_OK) return st;
-    launch_fn fn = lookup(c.pdt, c.adt, nmax_for(c.n), pl);
+    if ((st = make_plan(c.tokens, c.hidden, c.pdt, cus, &pl)) != ARF_OK) return st;
+    launch_fn fn = lookup(c.pdt, c.adt, c.n, pl);
     if (!fn) return ARF_ERR_VALUE;
     arf::Params p;
     p.partials = c.partials;
@@ -308,7 +329,7 @@ arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
         if (st != ARF_OK) return st;
     }
     Plan pl;
-    arf_status st = make_plan(tokens, hidden, num_cus, &pl);
+    arf_status st = make_plan(tokens, hidden, partial_dtype, num_cus, &pl);
     if (st != ARF_OK) return st;
     out[0] = pl.path;
     out[1] = pl.waves;

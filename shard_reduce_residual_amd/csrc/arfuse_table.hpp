@@ -1,64 +1,68 @@
 // arfuse_table.hpp -- the instantiated launch geometries of the fused kernel, and the
-// lookup from (shard bound, path, wavefronts per workgroup, chunks per lane) to a
-// launcher. One translation unit per (partial type, activation type) includes this.
+// lookup from (shard count, path, wavefronts per workgroup, chunks per lane) to a
+// launcher. Each inst_*.hip translation unit instantiates one element-type pair for a
+// range of shard counts, so the 1024 kernels compile in parallel.
 //
-// Menu: shard bound NMAX in {1, 2, 4, 8, 16}; one row per wavefront with 4 wavefronts
-// per workgroup and C in {1, 2, 4, 8}; one row per workgroup with WAVES in {2, 4, 8, 16}
-// and C in {1, 2, 4, 8}.
+// Menu: shard count N in 1..16 (exact: no per-shard branch, so the loads of a whole row
+// are scheduled freely); one row per wavefront (4 wavefronts per workgroup) with C in
+// {1, 2, 4, 8}; one row per workgroup with WAVES in {4, 8, 16} and C in {1, 2, 4, 8}.
 #pragma once
 
 #include "arfuse_device.hpp"
 
 namespace arf {
 
-template <class PT, class AT, int NM, int W>
+template <class PT, class AT, int N, int W>
 launch_fn pick_block_c(int c) {
     switch (c) {
-        case 1: return &launch_fused<PT, AT, NM, 1, W, false>;
-        case 2: return &launch_fused<PT, AT, NM, 2, W, false>;
-        case 4: return &launch_fused<PT, AT, NM, 4, W, false>;
-        case 8: return &launch_fused<PT, AT, NM, 8, W, false>;
+        case 1: return &launch_fused<PT, AT, N, 1, W, false>;
+        case 2: return &launch_fused<PT, AT, N, 2, W, false>;
+        case 4: return &launch_fused<PT, AT, N, 4, W, false>;
+        case 8: return &launch_fused<PT, AT, N, 8, W, false>;
         default: return nullptr;
     }
 }
 
-template <class PT, class AT, int NM>
+template <class PT, class AT, int N>
 launch_fn pick_geometry(bool row_per_wave, int waves, int c) {
     if (row_per_wave) {
         if (waves != 4) return nullptr;
         switch (c) {
-            case 1: return &launch_fused<PT, AT, NM, 1, 4, true>;
-            case 2: return &launch_fused<PT, AT, NM, 2, 4, true>;
-            case 4: return &launch_fused<PT, AT, NM, 4, 4, true>;
-            case 8: return &launch_fused<PT, AT, NM, 8, 4, true>;
+            case 1: return &launch_fused<PT, AT, N, 1, 4, true>;
+            case 2: return &launch_fused<PT, AT, N, 2, 4, true>;
+            case 4: return &launch_fused<PT, AT, N, 4, 4, true>;
+            case 8: return &launch_fused<PT, AT, N, 8, 4, true>;
             default: return nullptr;
         }
     }
     switch (waves) {
-        case 2: return pick_block_c<PT, AT, NM, 2>(c);
-        case 4: return pick_block_c<PT, AT, NM, 4>(c);
-        case 8: return pick_block_c<PT, AT, NM, 8>(c);
-        case 16: return pick_block_c<PT, AT, NM, 16>(c);
+        case 4: return pick_block_c<PT, AT, N, 4>(c);
+        case 8: return pick_block_c<PT, AT, N, 8>(c);
+        case 16: return pick_block_c<PT, AT, N, 16>(c);
         default: return nullptr;
     }
 }
 
-template <class PT, class AT>
-launch_fn pick_launcher(int nmax, bool row_per_wave, int waves, int c) {
-    switch (nmax) {
-        case 1: return pick_geometry<PT, AT, 1>(row_per_wave, waves, c);
-        case 2: return pick_geometry<PT, AT, 2>(row_per_wave, waves, c);
-        case 4: return pick_geometry<PT, AT, 4>(row_per_wave, waves, c);
-        case 8: return pick_geometry<PT, AT, 8>(row_per_wave, waves, c);
-        case 16: return pick_geometry<PT, AT, 16>(row_per_wave, waves, c);
-        default: return nullptr;
+template <class PT, class AT, int NLO, int NHI>
+launch_fn pick_shards(int n, bool row_per_wave, int waves, int c) {
+    if constexpr (NLO <= NHI) {
+        if (n == NLO) return pick_geometry<PT, AT, NLO>(row_per_wave, waves, c);
+        return pick_shards<PT, AT, NLO + 1, NHI>(n, row_per_wave, waves, c);
+    } else {
+        return nullptr;
     }
 }
 
-// Defined in the per-type translation units.
-launch_fn lookup_bf16_bf16(int nmax, bool row_per_wave, int waves, int c);
-launch_fn lookup_f16_f16(int nmax, bool row_per_wave, int waves, int c);
-launch_fn lookup_f32_bf16(int nmax, bool row_per_wave, int waves, int c);
-launch_fn lookup_f32_f16(int nmax, bool row_per_wave, int waves, int c);
+// Defined in the inst_<partial>_<activation>_n<lo>_<hi>.hip translation units.
+#define ARF_DECLARE_LOOKUPS(PD, AD)                                              \
+    launch_fn lookup_##PD##_##AD##_n01_04(int n, bool rpw, int waves, int c);    \
+    launch_fn lookup_##PD##_##AD##_n05_08(int n, bool rpw, int waves, int c);    \
+    launch_fn lookup_##PD##_##AD##_n09_12(int n, bool rpw, int waves, int c);    \
+    launch_fn lookup_##PD##_##AD##_n13_16(int n, bool rpw, int waves, int c);
+ARF_DECLARE_LOOKUPS(bf16, bf16)
+ARF_DECLARE_LOOKUPS(f16, f16)
+ARF_DECLARE_LOOKUPS(f32, bf16)
+ARF_DECLARE_LOOKUPS(f32, f16)
+#undef ARF_DECLARE_LOOKUPS
 
 }  // namespace arf

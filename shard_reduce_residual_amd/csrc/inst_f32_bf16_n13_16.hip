@@ -1,0 +1,8 @@
+// Instantiations of the fused kernel for partials PartF32, activations ActBF16, N = 13..16.
+#include "arfuse_table.hpp"
+
+namespace arf {
+launch_fn lookup_f32_bf16_n13_16(int n, bool rpw, int waves, int c) {
+    return pick_shards<PartF32, ActBF16, 13, 16>(n, rpw, waves, c);
+}
+}  // namespace arf

@@ -207,7 +207,7 @@ def _geometries(h):
     for c in (1, 2, 4, 8):
         if 64 * c >= hc:
             out.append((1, 4, c))
-        for wv in (2, 4, 8, 16):
+        for wv in (4, 8, 16):
             if wv * 64 * c >= hc:
                 out.append((2, wv, c))
     return out
