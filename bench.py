@@ -52,6 +52,68 @@ def read_traffic(workload_name: str):
     return float(kv["hbm_bytes_per_launch"])
 
 
+class Runner:
+    """Inputs and outputs of one workload on the GPU (``sets`` rotating copies) and the
+    launch of the fused path on ``stream``."""
+
+    def __init__(self, w, dev, stream, sets=1):
+        import torch
+
+        import workloads
+
+        self.w, self.stream = w, stream
+        t, h = w.tokens, w.hidden
+        adt = workloads.TORCH_DTYPES[w.act_dtype]
+        self.sets = []
+        for _ in range(sets):
+            p, r, g = workloads.generate(w, dev)
+            rout = torch.empty((t, h), dtype=adt, device=dev)
+            nout = torch.empty((t, h), dtype=adt, device=dev)
+            q = torch.empty((t, h), dtype=torch.uint8, device=dev) if w.quant else None
+            sc_out = (torch.empty((t,), dtype=torch.float32, device=dev)
+                      if w.quant == "per_token" else None)
+            # any positive per-tensor scale runs the same instructions
+            sc_in = (torch.tensor([0.01], dtype=torch.float32, device=dev)
+                     if w.quant == "per_tensor" else None)
+            self.sets.append((p, r, g, rout, nout, q, sc_out, sc_in))
+        self.k = 0
+
+    def step(self):
+        import shard_reduce_residual_amd as arf
+
+        w = self.w
+        p, r, g, rout, nout, q, sc_out, sc_in = self.sets[self.k % len(self.sets)]
+        self.k += 1
+        if w.quant is None:
+            arf.arf_reduce_add_rmsnorm(p, r, g, w.eps, residual_out=rout, norm_out=nout,
+                                       stream=self.stream)
+        else:
+            mode = (arf.ARF_QUANT_PER_TOKEN if w.quant == "per_token"
+                    else arf.ARF_QUANT_PER_TENSOR)
+            arf.arf_reduce_add_rmsnorm_quant(p, r, g, w.eps, q, mode, scale_in=sc_in,
+                                             scale_out=sc_out, residual_out=rout,
+                                             norm_out=nout, stream=self.stream)
+
+    def measure(self, steps, warmup):
+        """(wall ms per step, kernel ms per launch from events on the launch stream)."""
+        import torch
+
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(self.stream)
+        for _ in range(steps):
+            self.step()
+        ev1.record(self.stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return (t1 - t0) * 1e3 / steps, ev0.elapsed_time(ev1) / steps
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -61,6 +123,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target oracle time for the CPU baseline (0: skip it)")
     ap.add_argument("--no-copy-probe", action="store_true")
+    ap.add_argument("--secondary", default="c3",
+                    help="second workload reported in the 'secondary' object ('' for none)")
     return ap.parse_args()
 
 
@@ -73,7 +137,6 @@ def main():
               % (args.gpus, world), file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import shard_reduce_residual_amd as arf
@@ -82,49 +145,15 @@ def main():
     w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    t, h = w.tokens, w.hidden
-    adt = workloads.TORCH_DTYPES[w.act_dtype]
-    p, r, g = workloads.generate(w, dev)
-    rout = torch.empty((t, h), dtype=adt, device=dev)
-    nout = torch.empty((t, h), dtype=adt, device=dev)
-    q = torch.empty((t, h), dtype=torch.uint8, device=dev) if w.quant else None
-    sc_out = torch.empty((t,), dtype=torch.float32, device=dev) if w.quant == "per_token" else None
-    sc_in = None
-    if w.quant == "per_tensor":
-        # per-tensor scale of the first launch's own output is not the oracle's; for timing
-        # any positive scale exercises the same instructions
-        sc_in = torch.tensor([0.01], dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream(device=dev)
-
-    def step():
-        if w.quant is None:
-            arf.arf_reduce_add_rmsnorm(p, r, g, w.eps, residual_out=rout, norm_out=nout,
-                                       stream=stream)
-        else:
-            mode = arf.ARF_QUANT_PER_TOKEN if w.quant == "per_token" else arf.ARF_QUANT_PER_TENSOR
-            arf.arf_reduce_add_rmsnorm_quant(p, r, g, w.eps, q, mode, scale_in=sc_in,
-                                             scale_out=sc_out, residual_out=rout,
-                                             norm_out=nout, stream=stream)
-
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    t, h = w.tokens, w.hidden
+    run = Runner(w, dev, stream, sets=1)
+    ms_per_step, kernel_ms = run.measure(args.steps, args.warmup)
     B = w.algorithmic_bytes()
     value = B / (ms_per_step * 1e-3) / 1e9
     achieved = B / (kernel_ms * 1e-3) / 1e9
     traffic = read_traffic(w.name)
+    p, r, g, rout, nout, q, sc_out, sc_in = run.sets[0]
 
     # HBM ceiling probe: a streaming copy of 1 GiB with the same load/store forms
     copy = None
@@ -143,6 +172,26 @@ def main():
         torch.cuda.synchronize()
         copy = 2 * nb / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
         del src, dst
+
+    secondary = None
+    if args.secondary:
+        w2 = workloads.WORKLOADS[args.secondary]
+        B2 = w2.algorithmic_bytes()
+        # rotate enough buffer sets that the 256 MB Infinity Cache cannot serve a launch
+        sets = max(1, min(8, -(-1_500_000_000 // B2)))
+        run2 = Runner(w2, dev, stream, sets=sets)
+        steps2 = max(args.steps, 100)
+        ms2, kms2 = run2.measure(steps2, max(args.warmup, 10))
+        del run2
+        torch.cuda.empty_cache()
+        secondary = {"workload": w2.name, "buffer_sets": sets, "steps": steps2,
+                     "ms_per_step": round(ms2, 5), "kernel_ms": round(kms2, 5),
+                     "achieved": round(B2 / (kms2 * 1e-3) / 1e9, 2), "unit": "GB/s",
+                     "frac": round(B2 / (kms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "tokens_per_s": round(w2.tokens / (kms2 * 1e-3), 1),
+                     "plan": arf.arf_get_plan(w2.n_shards, w2.tokens, w2.hidden,
+                                              {"bf16": 0, "f16": 1, "f32": 2}[w2.partial_dtype]),
+                     "traffic": read_traffic(w2.name)}
 
     cpu = None
     parity = None
@@ -175,6 +224,7 @@ def main():
                      "traffic": traffic},
         "hbm_copy_ceiling_GBs": None if copy is None else round(copy, 1),
         "frac_of_copy_ceiling": None if copy is None else round(achieved / copy, 4),
+        "secondary": secondary,
         "cpu_baseline": cpu,
         "sample_parity": parity,
     }

@@ -175,11 +175,66 @@ __device__ __forceinline__ void load_partial_chunk(AT, u32x4 const (&v)[2], floa
     }
 }
 
+// Row layout of a lane's 8 elements in chunk j (G lanes per row, lane gl):
+//  * 16-bit partials: elements [8c, 8c+8) with c = j*G + gl -- one 16-byte access per
+//    shard and per 16-bit row, each wavefront instruction covering 1 KiB;
+//  * fp32 partials ("split"): two quads [4u, 4u+4) with u = (2j+w)*G + gl, w = 0, 1 --
+//    every 16-byte partial load is again 1 KiB contiguous per wavefront instruction
+//    (instead of 16 of every 32 bytes), and the 16-bit rows use 8-byte accesses.
+template <bool SPLIT, int G>
+struct Layout {
+    // byte offset of the w-th 16-byte partial piece of chunk j
+    __device__ static uint32_t part(int j, int w, int gl) {
+        return SPLIT ? (uint32_t)((2 * j + w) * G + gl) * 16u
+                     : (uint32_t)(j * G + gl) * 16u;
+    }
+    template <int AUX>
+    __device__ static u32x4 load_act(__amdgpu_buffer_rsrc_t r, int j, int gl) {
+        if constexpr (SPLIT) {
+            const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(
+                r, (uint32_t)((2 * j) * G + gl) * 8u, 0, AUX);
+            const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(
+                r, (uint32_t)((2 * j + 1) * G + gl) * 8u, 0, AUX);
+            return u32x4{a[0], a[1], b[0], b[1]};
+        } else {
+            return __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(j * G + gl) * 16u, 0,
+                                                         AUX);
+        }
+    }
+    __device__ static void store_act(u32x4 v, __amdgpu_buffer_rsrc_t r, int j, int gl) {
+        if constexpr (SPLIT) {
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{v[0], v[1]}, r,
+                                                  (uint32_t)((2 * j) * G + gl) * 8u, 0,
+                                                  kAuxStream);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{v[2], v[3]}, r,
+                                                  (uint32_t)((2 * j + 1) * G + gl) * 8u, 0,
+                                                  kAuxStream);
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, (uint32_t)(j * G + gl) * 16u, 0,
+                                                   kAuxStream);
+        }
+    }
+    // 8 fp8 codes of chunk j (q[0]: the first four elements, q[1]: the last four)
+    __device__ static void store_codes(u32x2 q, __amdgpu_buffer_rsrc_t r, int j, int gl) {
+        if constexpr (SPLIT) {
+            __builtin_amdgcn_raw_buffer_store_b32(q[0], r, (uint32_t)((2 * j) * G + gl) * 4u,
+                                                  0, kAuxStream);
+            __builtin_amdgcn_raw_buffer_store_b32(q[1], r,
+                                                  (uint32_t)((2 * j + 1) * G + gl) * 4u, 0,
+                                                  kAuxStream);
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b64(q, r, (uint32_t)(j * G + gl) * 8u, 0,
+                                                  kAuxStream);
+        }
+    }
+};
+
 template <class PT, class AT, int N, int C, int WAVES, bool ROW_PER_WAVE, int DEPTH = 2>
 __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p) {
     static_assert(N >= 1 && C >= 1 && DEPTH >= 2, "bad instantiation");
     constexpr int PW = PartTraits<PT>::kPieces;
     constexpr int G = ROW_PER_WAVE ? 64 : WAVES * 64;   // lanes per row
+    using L = Layout<(PW == 2), G>;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 
@@ -221,13 +276,11 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
 #pragma unroll
             for (int w = 0; w < PW; ++w)
                 buf[slot][j][w] = __builtin_amdgcn_raw_buffer_load_b128(
-                    part[r], (uint32_t)(j * G + gl) * (16u * PW) + 16u * w, 0, kAuxStream);
+                    part[r], L::part(j, w, gl), 0, kAuxStream);
     };
     auto issue_residual = [&]() {
 #pragma unroll
-        for (int j = 0; j < C; ++j)
-            rv[j] = __builtin_amdgcn_raw_buffer_load_b128(r_in, (uint32_t)(j * G + gl) * 16u, 0,
-                                                          kAuxStream);
+        for (int j = 0; j < C; ++j) rv[j] = L::template load_act<kAuxStream>(r_in, j, gl);
     };
 #pragma unroll
     for (int d = 0; d < DEPTH - 1; ++d)
@@ -258,8 +311,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
 #pragma unroll
         for (int e = 0; e < 8; ++e) sum[e] = s[e] + res[e];
         const u32x4 rr = pack8(AT{}, sum);       // residual_out
-        __builtin_amdgcn_raw_buffer_store_b128(rr, r_out, (uint32_t)(j * G + gl) * 16u, 0,
-                                               kAuxStream);
+        L::store_act(rr, r_out, j, gl);
         xr[j] = rr;
         float x[8];
         unpack8(AT{}, rr, x);
@@ -269,9 +321,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
 
     u32x4 gv[C];
 #pragma unroll
-    for (int j = 0; j < C; ++j)
-        gv[j] = __builtin_amdgcn_raw_buffer_load_b128(g_in, (uint32_t)(j * G + gl) * 16u, 0,
-                                                      kAuxDefault);
+    for (int j = 0; j < C; ++j) gv[j] = L::template load_act<kAuxDefault>(g_in, j, gl);
 
     // ---- mean of squares across the row
     ss = wave_sum(ss);
@@ -298,8 +348,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
             y[e] = v * g[e];
         }
         const u32x4 yr = pack8(AT{}, y);
-        __builtin_amdgcn_raw_buffer_store_b128(yr, y_out, (uint32_t)(j * G + gl) * 16u, 0,
-                                               kAuxStream);
+        L::store_act(yr, y_out, j, gl);
         xr[j] = yr;
         if (p.quant_mode == kQuantToken) {
             float yc[8];
@@ -336,8 +385,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
         u32x2 q;
         q[0] = e4m3x4(y[0] * inv_scale, y[1] * inv_scale, y[2] * inv_scale, y[3] * inv_scale);
         q[1] = e4m3x4(y[4] * inv_scale, y[5] * inv_scale, y[6] * inv_scale, y[7] * inv_scale);
-        __builtin_amdgcn_raw_buffer_store_b64(q, q_out, (uint32_t)(j * G + gl) * 8u, 0,
-                                              kAuxStream);
+        L::store_codes(q, q_out, j, gl);
     }
 }
 

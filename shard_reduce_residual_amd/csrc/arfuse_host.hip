@@ -44,10 +44,9 @@ int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //  * otherwise one row per workgroup:
 //    - few rows (< 2 per compute unit): 8 wavefronts per row, so that each row exposes
 //      more parallel loads;
-//    - fp32 partials: 16 wavefronts, one chunk per lane where the row allows;
 //    - otherwise 4 wavefronts with up to 8 chunks per lane, so that several rows share a
 //      compute unit; rows above 2048 chunks use 16 wavefronts.
-arf_status make_plan(int64_t tokens, int32_t hidden, int32_t pdt, int num_cus, Plan* pl) {
+arf_status make_plan(int64_t tokens, int32_t hidden, int num_cus, Plan* pl) {
     const int hc = hidden / 8;
     int path = g_path.load(), waves = g_waves.load(), chunks = g_chunks.load();
     if (path == 0) {
@@ -57,13 +56,7 @@ arf_status make_plan(int64_t tokens, int32_t hidden, int32_t pdt, int num_cus, P
             path = 1;
         } else {
             path = 2;
-            if (!many_rows) {
-                waves = 8;
-            } else if (pdt == ARF_F32) {
-                waves = 16;
-            } else {
-                waves = 4;
-            }
+            waves = many_rows ? 4 : 8;
             if (hc > waves * 64 * 8) waves = 16;
             chunks = pow2_at_least(div_up(hc, waves * 64));
         }
@@ -203,7 +196,7 @@ arf_status run(const Call& c, void* stream) {
     int cus = 0;
     if ((st = device_cus(&cus)) != ARF_OK) return st;
     Plan pl;
-    if ((st = make_plan(c.tokens, c.hidden, c.pdt, cus, &pl)) != ARF_OK) return st;
+    if ((st = make_plan(c.tokens, c.hidden, cus, &pl)) != ARF_OK) return st;
     launch_fn fn = lookup(c.pdt, c.adt, c.n, pl);
     if (!fn) return ARF_ERR_VALUE;
     arf::Params p;
@@ -329,7 +322,7 @@ arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
         if (st != ARF_OK) return st;
     }
     Plan pl;
-    arf_status st = make_plan(tokens, hidden, partial_dtype, num_cus, &pl);
+    arf_status st = make_plan(tokens, hidden, num_cus, &pl);
     if (st != ARF_OK) return st;
     out[0] = pl.path;
     out[1] = pl.waves;
@@ -377,7 +370,7 @@ arf_status arf_stream_copy(void* dst, const void* src, int64_t bytes, void* stre
     arf_status st = device_cus(&cus);
     if (st != ARF_OK) return st;
     const int64_t spans = (bytes + kCopySpan - 1) / kCopySpan;
-    const int64_t cap = (int64_t)cus * 8;
+    const int64_t cap = (int64_t)cus * 16;
     const uint32_t grid = (uint32_t)(spans < cap ? spans : cap);
     char* d = (char*)dst;
     const char* s = (const char*)src;

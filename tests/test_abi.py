@@ -134,7 +134,7 @@ def test_plan_covers_the_row_and_follows_the_menu():
 def test_plan_for_the_named_workloads():
     # geometries measured best on MI355X for these shapes
     assert plan(8, 8192, 16384) == {"path": 2, "waves": 4, "chunks": 8, "grid": 8192}
-    assert plan(4, 2048, 7168, 2) == {"path": 2, "waves": 16, "chunks": 1, "grid": 2048}
+    assert plan(4, 2048, 7168, 2) == {"path": 2, "waves": 4, "chunks": 4, "grid": 2048}
     assert plan(8, 128, 4096) == {"path": 2, "waves": 8, "chunks": 1, "grid": 128}
     assert plan(8, 64, 8192) == {"path": 2, "waves": 8, "chunks": 2, "grid": 64}
     assert plan(2, 16, 1024)["path"] == 2
