@@ -28,6 +28,21 @@ _LIB = os.path.join(_HERE, "libarf_oracle.so")
 
 DTYPES = {"bf16": 0, "f16": 1, "f32": 2}
 MODES = {"per_tensor": 0, "per_token": 1}
+ACCUMULATE = {"f32": 0, "partial": 1}
+
+
+class Args(ctypes.Structure):
+    """Mirror of ``arfo_args`` in arf_oracle.h."""
+    _fields_ = [("partials", ctypes.c_void_p), ("n_shards", ctypes.c_int32),
+                ("tokens", ctypes.c_int64), ("hidden", ctypes.c_int32),
+                ("partial_dtype", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("accumulate", ctypes.c_int32), ("row_begin", ctypes.c_int64),
+                ("row_count", ctypes.c_int64), ("residual_in", ctypes.c_void_p),
+                ("residual_out", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("eps", ctypes.c_float), ("norm_out", ctypes.c_void_p),
+                ("quant_out", ctypes.c_void_p), ("quant_mode", ctypes.c_int32),
+                ("scale_in", ctypes.c_void_p), ("scale_out", ctypes.c_void_p),
+                ("n_threads", ctypes.c_int32)]
 
 
 def build(force: bool = False) -> str:
@@ -72,6 +87,10 @@ def lib() -> ctypes.CDLL:
         L.arfo_reduce_add_rmsnorm_quant.argtypes = [vp, i32, i64, i32, i32, i32, vp, vp, vp,
                                                     f32, vp, vp, i32, vp, vp, i32]
         L.arfo_reduce_add_rmsnorm_quant.restype = ctypes.c_int
+        L.arfo_run.argtypes = [ctypes.POINTER(Args)]
+        L.arfo_run.restype = ctypes.c_int
+        L.arfo_reduce_rows.argtypes = [vp, i32, i64, i32, i32, i32, i32, i64, i64, vp, i32]
+        L.arfo_reduce_rows.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -142,52 +161,81 @@ def reduce_add_rmsnorm(partials: np.ndarray, residual_in: np.ndarray, gamma: np.
                        residual_out: bool = True, norm_out: bool = True,
                        quant: str | None = None, scale_in: float | None = None,
                        residual_out_array: np.ndarray | None = None,
+                       accumulate: str = "f32", rows: tuple | None = None,
+                       out_init: int | None = None,
                        n_threads: int | None = None) -> dict:
     """Run the oracle. ``partials`` is [N][T][H] (uint16 bits or float32),
     ``residual_in`` [T][H] uint16 bits, ``gamma`` [H] uint16 bits.
 
     Returns a dict with ``residual_out`` / ``norm_out`` (uint16 bits), ``quant_out``
     (uint8 codes) and ``scale_out`` (float32 [T], per-token mode) as requested.
-    ``residual_out_array`` may be ``residual_in`` itself to run in place.
+    ``residual_out_array`` may be ``residual_in`` itself to run in place. ``accumulate``
+    is "f32" (the default branch) or "partial" (rounded to the partial type after every
+    addition). ``rows`` = (begin, count) restricts the computed rows; output rows outside
+    it keep ``out_init`` (a byte value, default 0).
     """
     n, t, h = partials.shape
-    pd = DTYPES[partial_dtype]
-    ad = DTYPES[act_dtype]
     want_p = np.float32 if partial_dtype == "f32" else np.uint16
     partials = np.ascontiguousarray(partials, dtype=want_p)
     if residual_out_array is None:
         residual_in = np.ascontiguousarray(residual_in, dtype=np.uint16)
     gamma = np.ascontiguousarray(gamma, dtype=np.uint16)
     assert residual_in.shape == (t, h) and gamma.shape == (h,)
+    fill = 0 if out_init is None else out_init
+
+    def new(shape, dtype):
+        a = np.empty(shape, dtype)
+        a.view(np.uint8)[...] = fill
+        return a
+
     out = {}
     if residual_out_array is not None:
         rout = residual_out_array
         out["residual_out"] = rout
     else:
-        rout = np.empty((t, h), np.uint16) if residual_out else None
+        rout = new((t, h), np.uint16) if residual_out else None
         if rout is not None:
             out["residual_out"] = rout
-    nout = np.empty((t, h), np.uint16) if norm_out else None
+    nout = new((t, h), np.uint16) if norm_out else None
     if nout is not None:
         out["norm_out"] = nout
     thr = default_threads() if n_threads is None else n_threads
-    if quant is None:
-        rc = lib().arfo_reduce_add_rmsnorm(_ptr(partials), n, t, h, pd, ad, _ptr(residual_in),
-                                           _ptr(rout), _ptr(gamma), eps, _ptr(nout), thr)
-    else:
-        q = np.empty((t, h), np.uint8)
+    q = sin = sout = None
+    mode = -1
+    if quant is not None:
+        mode = MODES[quant]
+        q = new((t, h), np.uint8)
         out["quant_out"] = q
-        sin = None
-        sout = None
         if quant == "per_tensor":
             sin = np.array([scale_in], np.float32)
         else:
-            sout = np.empty((t,), np.float32)
+            sout = new((t,), np.float32)
             out["scale_out"] = sout
-        rc = lib().arfo_reduce_add_rmsnorm_quant(_ptr(partials), n, t, h, pd, ad,
-                                                 _ptr(residual_in), _ptr(rout), _ptr(gamma),
-                                                 eps, _ptr(nout), _ptr(q), MODES[quant],
-                                                 _ptr(sin), _ptr(sout), thr)
+    begin, count = (0, -1) if rows is None else rows
+    a = Args(_ptr(partials), n, t, h, DTYPES[partial_dtype], DTYPES[act_dtype],
+             ACCUMULATE[accumulate], begin, count, _ptr(residual_in), _ptr(rout), _ptr(gamma),
+             eps, _ptr(nout), _ptr(q), mode, _ptr(sin), _ptr(sout), thr)
+    rc = lib().arfo_run(ctypes.byref(a))
     if rc != 0:
         raise OracleError("oracle rejected the arguments (code %d)" % rc)
     return out
+
+
+def reduce_rows(partials: np.ndarray, *, partial_dtype: str, act_dtype: str,
+                accumulate: str = "f32", rows: tuple | None = None,
+                out_init: int = 0, n_threads: int | None = None) -> np.ndarray:
+    """The reduced value (cast to the activation type) of rows (begin, count) of
+    [N][T][H] partials, as a [T][H] uint16 array; other rows keep ``out_init`` bytes."""
+    n, t, h = partials.shape
+    want_p = np.float32 if partial_dtype == "f32" else np.uint16
+    partials = np.ascontiguousarray(partials, dtype=want_p)
+    sums = np.empty((t, h), np.uint16)
+    sums.view(np.uint8)[...] = out_init
+    begin, count = (0, -1) if rows is None else rows
+    thr = default_threads() if n_threads is None else n_threads
+    rc = lib().arfo_reduce_rows(_ptr(partials), n, t, h, DTYPES[partial_dtype],
+                                DTYPES[act_dtype], ACCUMULATE[accumulate], begin, count,
+                                _ptr(sums), thr)
+    if rc != 0:
+        raise OracleError("oracle rejected the arguments (code %d)" % rc)
+    return sums

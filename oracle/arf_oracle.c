@@ -13,6 +13,8 @@
  * hidden index i. Sources:
  *   [SUM]   TensorRT-LLM page "allReduceFusionKernels.cu", function allreduce_sum,
  *           fp32-accumulation branch (the default per use_fp32_acc).
+ *   [SUM-P] same function, other branch: the packs are added with add128 in DType, so
+ *           every partial sum is rounded to the partial type.
  *   [ADD]   same page, fused_op and add128 (residual add in the activation type).
  *   [NORM]  same page, rms_norm.
  *   [LAYOUT] same page, oneshot-sync kernel post-barrier loop (shard r of a token's
@@ -189,6 +191,8 @@ typedef struct {
     int64_t tokens;
     int32_t hidden;
     int32_t pdt, adt;
+    int32_t acc;              /* ARFO_ACC_F32 | ARFO_ACC_PARTIAL */
+    uint16_t* sums_out;       /* reduce only when non-NULL */
     const uint16_t* residual_in;
     uint16_t* residual_out;
     const uint16_t* gamma;
@@ -200,19 +204,41 @@ typedef struct {
     float* scale_out;
 } job_t;
 
+/* Round an fp32 value to the partial type (identity for fp32 partials). */
+static float to_partial_type(float x, int32_t pdt)
+{
+    if (pdt == ARFO_F32) return x;
+    return act_to_f32(f32_to_act(x, pdt), pdt);
+}
+
+/* O1-O2 for one element: the reduced value in the activation type. */
+static uint16_t reduce_element(const job_t* j, int64_t shard_stride, int64_t idx)
+{
+    /* O1 [SUM]: start from rank 0's value and add ranks 1..N-1 one at a time, in fp32;
+       or [SUM-P] in the partial type: each partial sum is rounded to that type. One fp32
+       addition followed by one rounding to a p-bit type gives the correctly rounded sum
+       of the two values, since 24 >= 2p + 2 (double rounding is innocuous). */
+    float acc = partial_at(j->partials, j->pdt, idx);
+    for (int32_t r = 1; r < j->n_shards; ++r) {
+        acc = acc + partial_at(j->partials, j->pdt, (int64_t)r * shard_stride + idx);
+        if (j->acc == ARFO_ACC_PARTIAL) acc = to_partial_type(acc, j->pdt);
+    }
+    /* O2 [SUM]: the reduced value is cast back to the activation type. */
+    return f32_to_act(acc, j->adt);
+}
+
 static void one_token(const job_t* j, int64_t t, uint16_t* rrow, uint16_t* yrow)
 {
     const int64_t H = j->hidden;
     const int64_t shard_stride = j->tokens * H;      /* [LAYOUT]: dense [N][T][H] */
     const int64_t row = t * H;
 
+    if (j->sums_out) {
+        for (int64_t i = 0; i < H; ++i) j->sums_out[row + i] = reduce_element(j, shard_stride, row + i);
+        return;
+    }
     for (int64_t i = 0; i < H; ++i) {
-        /* O1 [SUM]: start from rank 0's value, add ranks 1..N-1 one at a time in fp32. */
-        float acc = partial_at(j->partials, j->pdt, row + i);
-        for (int32_t r = 1; r < j->n_shards; ++r)
-            acc = acc + partial_at(j->partials, j->pdt, (int64_t)r * shard_stride + row + i);
-        /* O2 [SUM]: the reduced value is cast back to the activation type. */
-        uint16_t s = f32_to_act(acc, j->adt);
+        uint16_t s = reduce_element(j, shard_stride, row + i);
         /* O3 [ADD]: residual add in the activation type: the exact sum of two 16-bit
            values, rounded once (one binary32 add is exact-then-rounded to 24 bits and a
            second rounding to 8 or 11 bits cannot differ from a direct one, since
@@ -291,18 +317,18 @@ static void* run_slice(void* arg)
     return NULL;
 }
 
-static int run_job(const job_t* j, int32_t n_threads)
+static int run_job(const job_t* j, int64_t row_begin, int64_t row_count, int32_t n_threads)
 {
-    if (j->tokens == 0) return ARFO_OK;
+    if (row_count == 0) return ARFO_OK;
     if (n_threads < 1) n_threads = 1;
-    if ((int64_t)n_threads > j->tokens) n_threads = (int32_t)j->tokens;
+    if ((int64_t)n_threads > row_count) n_threads = (int32_t)row_count;
     slice_t* sl = (slice_t*)calloc((size_t)n_threads, sizeof(slice_t));
     pthread_t* th = (pthread_t*)calloc((size_t)n_threads, sizeof(pthread_t));
     if (!sl || !th) { free(sl); free(th); return ARFO_ERR_VALUE; }
     for (int32_t k = 0; k < n_threads; ++k) {
         sl[k].job = j;
-        sl[k].t0 = j->tokens * k / n_threads;
-        sl[k].t1 = j->tokens * (k + 1) / n_threads;
+        sl[k].t0 = row_begin + row_count * k / n_threads;
+        sl[k].t1 = row_begin + row_count * (k + 1) / n_threads;
     }
     int failed = 0;
     for (int32_t k = 1; k < n_threads; ++k)
@@ -319,15 +345,70 @@ static int run_job(const job_t* j, int32_t n_threads)
 }
 
 static int check_common(const void* partials, int32_t n_shards, int64_t tokens,
-                        int32_t hidden, int32_t pdt, int32_t adt, const void* residual_in,
-                        const void* gamma, float eps)
+                        int32_t hidden, int32_t pdt, int32_t adt, int32_t acc, float eps)
 {
-    if (!partials || !residual_in || !gamma) return ARFO_ERR_NULL;
+    if (!partials) return ARFO_ERR_NULL;
     if (n_shards < 1 || tokens < 0 || hidden < 1) return ARFO_ERR_SHAPE;
     if (adt != ARFO_BF16 && adt != ARFO_F16) return ARFO_ERR_DTYPE;
     if (pdt != ARFO_BF16 && pdt != ARFO_F16 && pdt != ARFO_F32) return ARFO_ERR_DTYPE;
+    if (acc != ARFO_ACC_F32 && acc != ARFO_ACC_PARTIAL) return ARFO_ERR_VALUE;
     if (!(eps >= 0.0f) || isinf(eps)) return ARFO_ERR_VALUE;
     return ARFO_OK;
+}
+
+/* Resolve a row range against [0, tokens); returns 0 on success. */
+static int resolve_rows(int64_t tokens, int64_t begin, int64_t count, int64_t* b, int64_t* c)
+{
+    if (begin < 0 || begin > tokens) return ARFO_ERR_SHAPE;
+    if (count < 0) count = tokens - begin;
+    if (count > tokens - begin) return ARFO_ERR_SHAPE;
+    *b = begin;
+    *c = count;
+    return ARFO_OK;
+}
+
+int arfo_run(const arfo_args* a)
+{
+    if (!a) return ARFO_ERR_NULL;
+    int rc = check_common(a->partials, a->n_shards, a->tokens, a->hidden, a->partial_dtype,
+                          a->act_dtype, a->accumulate, a->eps);
+    if (rc) return rc;
+    if (!a->residual_in || !a->gamma) return ARFO_ERR_NULL;
+    if (a->quant_mode < 0) {
+        if (!a->residual_out && !a->norm_out) return ARFO_ERR_NULL;
+    } else {
+        if (!a->quant_out) return ARFO_ERR_NULL;
+        if (a->quant_mode == ARFO_PER_TENSOR) {
+            if (!a->scale_in) return ARFO_ERR_NULL;
+        } else if (a->quant_mode == ARFO_PER_TOKEN) {
+            if (!a->scale_out) return ARFO_ERR_NULL;
+        } else {
+            return ARFO_ERR_VALUE;
+        }
+    }
+    int64_t b, c;
+    if ((rc = resolve_rows(a->tokens, a->row_begin, a->row_count, &b, &c))) return rc;
+    job_t j = {a->partials, a->n_shards, a->tokens, a->hidden, a->partial_dtype, a->act_dtype,
+               a->accumulate, NULL, (const uint16_t*)a->residual_in,
+               (uint16_t*)a->residual_out, (const uint16_t*)a->gamma, a->eps,
+               (uint16_t*)a->norm_out, a->quant_mode < 0 ? NULL : a->quant_out,
+               a->quant_mode < 0 ? 0 : a->quant_mode, a->scale_in, a->scale_out};
+    return run_job(&j, b, c, a->n_threads);
+}
+
+int arfo_reduce_rows(const void* partials, int32_t n_shards, int64_t tokens, int32_t hidden,
+                     int32_t partial_dtype, int32_t act_dtype, int32_t accumulate,
+                     int64_t row_begin, int64_t row_count, void* sums_out, int32_t n_threads)
+{
+    int rc = check_common(partials, n_shards, tokens, hidden, partial_dtype, act_dtype,
+                          accumulate, 0.0f);
+    if (rc) return rc;
+    if (!sums_out) return ARFO_ERR_NULL;
+    int64_t b, c;
+    if ((rc = resolve_rows(tokens, row_begin, row_count, &b, &c))) return rc;
+    job_t j = {partials, n_shards, tokens, hidden, partial_dtype, act_dtype, accumulate,
+               (uint16_t*)sums_out, NULL, NULL, NULL, 0.0f, NULL, NULL, 0, NULL, NULL};
+    return run_job(&j, b, c, n_threads);
 }
 
 int arfo_reduce_add_rmsnorm(const void* partials, int32_t n_shards, int64_t tokens,
@@ -335,14 +416,10 @@ int arfo_reduce_add_rmsnorm(const void* partials, int32_t n_shards, int64_t toke
                             const void* residual_in, void* residual_out, const void* gamma,
                             float eps, void* norm_out, int32_t n_threads)
 {
-    int rc = check_common(partials, n_shards, tokens, hidden, partial_dtype, act_dtype,
-                          residual_in, gamma, eps);
-    if (rc) return rc;
-    if (!residual_out && !norm_out) return ARFO_ERR_NULL;
-    job_t j = {partials, n_shards, tokens, hidden, partial_dtype, act_dtype,
-               (const uint16_t*)residual_in, (uint16_t*)residual_out,
-               (const uint16_t*)gamma, eps, (uint16_t*)norm_out, NULL, 0, NULL, NULL};
-    return run_job(&j, n_threads);
+    arfo_args a = {partials, n_shards, tokens, hidden, partial_dtype, act_dtype, ARFO_ACC_F32,
+                   0, -1, residual_in, residual_out, gamma, eps, norm_out, NULL, -1, NULL,
+                   NULL, n_threads};
+    return arfo_run(&a);
 }
 
 int arfo_reduce_add_rmsnorm_quant(const void* partials, int32_t n_shards, int64_t tokens,
@@ -352,20 +429,13 @@ int arfo_reduce_add_rmsnorm_quant(const void* partials, int32_t n_shards, int64_
                                   uint8_t* quant_out, int32_t mode, const float* scale_in,
                                   float* scale_out, int32_t n_threads)
 {
-    int rc = check_common(partials, n_shards, tokens, hidden, partial_dtype, act_dtype,
-                          residual_in, gamma, eps);
-    if (rc) return rc;
-    if (!quant_out) return ARFO_ERR_NULL;
-    if (mode == ARFO_PER_TENSOR) {
-        if (!scale_in) return ARFO_ERR_NULL;
-    } else if (mode == ARFO_PER_TOKEN) {
-        if (!scale_out) return ARFO_ERR_NULL;
-    } else {
-        return ARFO_ERR_VALUE;
+    if (mode != ARFO_PER_TENSOR && mode != ARFO_PER_TOKEN) {
+        int rc = check_common(partials, n_shards, tokens, hidden, partial_dtype, act_dtype,
+                              ARFO_ACC_F32, eps);
+        return rc ? rc : ARFO_ERR_VALUE;
     }
-    job_t j = {partials, n_shards, tokens, hidden, partial_dtype, act_dtype,
-               (const uint16_t*)residual_in, (uint16_t*)residual_out,
-               (const uint16_t*)gamma, eps, (uint16_t*)norm_out, quant_out, mode,
-               scale_in, scale_out};
-    return run_job(&j, n_threads);
+    arfo_args a = {partials, n_shards, tokens, hidden, partial_dtype, act_dtype, ARFO_ACC_F32,
+                   0, -1, residual_in, residual_out, gamma, eps, norm_out, quant_out, mode,
+                   scale_in, scale_out, n_threads};
+    return arfo_run(&a);
 }

@@ -26,6 +26,9 @@ extern "C" {
 
 /* Element types, as seen by the oracle. */
 enum { ARFO_BF16 = 0, ARFO_F16 = 1, ARFO_F32 = 2 };
+/* Accumulation of the shards: fp32 (the page's default), or in the partial type with a
+   rounding after every addition (the page's other branch, add128 in DType). */
+enum { ARFO_ACC_F32 = 0, ARFO_ACC_PARTIAL = 1 };
 /* fp8 scale modes. */
 enum { ARFO_PER_TENSOR = 0, ARFO_PER_TOKEN = 1 };
 /* Error codes. */
@@ -70,6 +73,43 @@ int arfo_reduce_add_rmsnorm_quant(const void* partials, int32_t n_shards, int64_
                                   const void* gamma, float eps, void* norm_out,
                                   uint8_t* quant_out, int32_t mode, const float* scale_in,
                                   float* scale_out, int32_t n_threads);
+
+/*
+ * General form. Rows [row_begin, row_begin + row_count) of the [tokens] rows are computed
+ * (row_count < 0: to the end); every buffer keeps its full [tokens] layout and rows outside
+ * the range are neither read nor written. quant_mode < 0: no fp8 copy.
+ */
+typedef struct arfo_args {
+    const void* partials;
+    int32_t n_shards;
+    int64_t tokens;
+    int32_t hidden;
+    int32_t partial_dtype;
+    int32_t act_dtype;
+    int32_t accumulate;
+    int64_t row_begin;
+    int64_t row_count;
+    const void* residual_in;
+    void* residual_out;
+    const void* gamma;
+    float eps;
+    void* norm_out;
+    uint8_t* quant_out;
+    int32_t quant_mode;
+    const float* scale_in;
+    float* scale_out;
+    int32_t n_threads;
+} arfo_args;
+
+int arfo_run(const arfo_args* a);
+
+/*
+ * Reduce only (one rank's share of the token-slice exchange): sums_out[t][i] = the
+ * reduced value cast to act_dtype, for rows t in [row_begin, row_begin + row_count).
+ */
+int arfo_reduce_rows(const void* partials, int32_t n_shards, int64_t tokens, int32_t hidden,
+                     int32_t partial_dtype, int32_t act_dtype, int32_t accumulate,
+                     int64_t row_begin, int64_t row_count, void* sums_out, int32_t n_threads);
 
 #ifdef __cplusplus
 }
