@@ -123,6 +123,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target oracle time for the CPU baseline (0: skip it)")
     ap.add_argument("--no-copy-probe", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the accumulation and token-slice variants")
     ap.add_argument("--secondary", default="c3",
                     help="second workload reported in the 'secondary' object ('' for none)")
     return ap.parse_args()
@@ -195,8 +197,12 @@ def main():
 
     cpu = None
     parity = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0:   # before the variants, which overwrite the outputs
         cpu, parity = cpu_baseline(args, w, p, r, g, rout, nout, q, sc_out, sc_in)
+
+    variants = None
+    if not args.no_variants:
+        variants = measure_variants(w, run, stream, max(args.steps, 10), args.warmup)
 
     plan = arf.arf_get_plan(w.n_shards, t, h, {"bf16": 0, "f16": 1, "f32": 2}[w.partial_dtype])
     line = {
@@ -225,11 +231,79 @@ def main():
         "hbm_copy_ceiling_GBs": None if copy is None else round(copy, 1),
         "frac_of_copy_ceiling": None if copy is None else round(achieved / copy, 4),
         "secondary": secondary,
+        "variants": variants,
         "cpu_baseline": cpu,
         "sample_parity": parity,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def _events_ms(fn, stream, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def measure_variants(w, run, stream, steps, warmup):
+    """The same workload with accumulation in the partial type, and one rank's share of
+    the token-slice exchange (reduce T/N rows of the N shards; then the epilogue over
+    all T rows from the gathered reduced values, as one shard)."""
+    import torch
+
+    import shard_reduce_residual_amd as arf
+
+    p, r, g, rout, nout, q, sc_out, sc_in = run.sets[0]
+    t, h, n = w.tokens, w.hidden, w.n_shards
+    mode = arf.ARF_QUANT_PER_TOKEN if w.quant == "per_token" else arf.ARF_QUANT_PER_TENSOR
+    quant = dict(quant_out=q, mode=mode, scale_in=sc_in, scale_out=sc_out) if w.quant else {}
+    B = w.algorithmic_bytes()
+    out = {}
+
+    def acc_partial():
+        arf.arf_fused_epilogue(p, r, g, w.eps, residual_out=rout, norm_out=nout,
+                               accumulate=arf.ARF_ACC_PARTIAL, stream=stream, **quant)
+
+    ms = _events_ms(acc_partial, stream, steps, warmup)
+    out["accumulate_partial"] = {"kernel_ms": round(ms, 5),
+                                 "achieved": round(B / (ms * 1e-3) / 1e9, 2)}
+
+    sums = torch.empty((t, h), dtype=rout.dtype, device=rout.device)
+    cnt = t // n + (1 if t % n else 0)   # rank 0's slice (the largest)
+
+    def reduce_slice():
+        arf.arf_reduce_rows(p, sums, row_begin=0, row_count=cnt, stream=stream)
+
+    def epilogue():
+        arf.arf_reduce_add_rmsnorm_quant(sums.view(1, t, h), r, g, w.eps, q, mode,
+                                         scale_in=sc_in, scale_out=sc_out, residual_out=rout,
+                                         norm_out=nout, stream=stream) if w.quant else \
+            arf.arf_reduce_add_rmsnorm(sums.view(1, t, h), r, g, w.eps, residual_out=rout,
+                                       norm_out=nout, stream=stream)
+
+    arf.arf_reduce_rows(p, sums, stream=stream)   # every row holds a reduced value
+    ms_r = _events_ms(reduce_slice, stream, steps, warmup)
+    ms_e = _events_ms(epilogue, stream, steps, warmup)
+    sp = w.sp
+    b_r = n * cnt * h * sp + cnt * h * 2
+    b_e = w.with_tokens(t).algorithmic_bytes() - n * t * h * sp + t * h * 2
+    out["token_slice_share"] = {
+        "slice_rows": cnt, "reduce_ms": round(ms_r, 5),
+        "reduce_achieved": round(b_r / (ms_r * 1e-3) / 1e9, 2),
+        "epilogue_ms": round(ms_e, 5), "epilogue_achieved": round(b_e / (ms_e * 1e-3) / 1e9, 2),
+        "unit": "GB/s"}
+    del sums
+    return out
 
 
 def cpu_baseline(args, w, p, r, g, rout, nout, q, sc_out, sc_in):

@@ -42,12 +42,19 @@
 extern "C" {
 #endif
 
-#define ARF_VERSION 100 /* 0.1.0 */
+#define ARF_VERSION 200 /* 0.2.0 */
 
 /* Element types (arguments typed int32_t take these values). */
 #define ARF_BF16 0
 #define ARF_F16 1
 #define ARF_F32 2
+
+/* Accumulation of the shards (allreduce_sum on the TensorRT-LLM page has both):
+   ARF_ACC_F32: fp32 adds in rank order, one cast at the end (the page's default);
+   ARF_ACC_PARTIAL: every partial sum is rounded to the partial type (add128 in DType);
+   identical to ARF_ACC_F32 for fp32 partials. */
+#define ARF_ACC_F32 0
+#define ARF_ACC_PARTIAL 1
 
 /* fp8 scale modes. */
 #define ARF_QUANT_PER_TENSOR 0 /* y ~ code * scale_in[0], scale given by the caller */
@@ -61,14 +68,16 @@ typedef enum arf_status {
     ARF_OK = 0,
     ARF_ERR_NULL = 1,      /* a required pointer is NULL                                  */
     ARF_ERR_SHAPE = 2,     /* n_shards not in 1..16, tokens < 0 or > 2^31-1, hidden not a
-                              positive multiple of 8 or above ARF_MAX_HIDDEN                */
+                              positive multiple of 8 or above ARF_MAX_HIDDEN, or a row
+                              range outside [0, tokens)                                    */
     ARF_ERR_DTYPE = 3,     /* act_dtype not BF16/F16, or partial_dtype neither act_dtype
                               nor F32                                                      */
     ARF_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned (scales: 4-byte)      */
     ARF_ERR_ALIAS = 5,     /* an output overlaps another buffer (the only overlap allowed
                               is residual_out == residual_in exactly)                      */
     ARF_ERR_NO_OUTPUT = 6, /* residual_out and norm_out are both NULL (non-quant entry)    */
-    ARF_ERR_VALUE = 7,     /* eps negative or not finite; unknown quant mode; bad override */
+    ARF_ERR_VALUE = 7,     /* eps negative or not finite; unknown quant or accumulation
+                              mode; bad override; wrong struct_size                        */
     ARF_ERR_HIP = 8        /* no usable device, or the kernel launch failed               */
 } arf_status;
 
@@ -112,6 +121,57 @@ arf_status arf_reduce_add_rmsnorm_quant(const void* partials, int32_t n_shards,
                                         uint8_t* quant_out, int32_t mode,
                                         const float* scale_in, float* scale_out,
                                         void* stream);
+
+/*
+ * General form of the two calls above, mirroring the page's parameter block
+ * (AllReduceFusionParams): the same buffers, plus
+ *   struct_size  must be sizeof(arf_params) (a newer or older layout is ARF_ERR_VALUE);
+ *   row_begin,   rows [row_begin, row_begin + row_count) are computed (row_count < 0:
+ *   row_count    through row tokens-1). Every buffer keeps its full [tokens] layout, the
+ *                partials their shard stride tokens*hidden; rows outside the range are
+ *                neither read nor written. 0 <= row_begin <= tokens.
+ *   accumulate   ARF_ACC_F32 or ARF_ACC_PARTIAL.
+ *   quant_out    NULL for no quantised copy; else quant_mode, scale_in and scale_out as
+ *                in arf_reduce_add_rmsnorm_quant.
+ */
+typedef struct arf_params {
+    uint32_t struct_size;
+    int32_t n_shards;
+    const void* partials;
+    int64_t tokens;
+    int64_t row_begin;
+    int64_t row_count;
+    int32_t hidden;
+    int32_t partial_dtype;
+    int32_t act_dtype;
+    int32_t accumulate;
+    const void* residual_in;
+    void* residual_out;
+    const void* gamma;
+    float eps;
+    void* norm_out;
+    uint8_t* quant_out;
+    int32_t quant_mode;
+    const float* scale_in;
+    float* scale_out;
+} arf_params;
+
+arf_status arf_fused_epilogue(const arf_params* params, void* stream);
+
+/*
+ * Reduce only: one rank's share of the token-slice (twoshot) exchange on the TensorRT-LLM
+ * page, where a rank reduces its slice of tokens, all ranks exchange the reduced values,
+ * and each then runs the epilogue over all tokens (arf_reduce_add_rmsnorm with
+ * n_shards = 1 on the gathered values gives exactly the oneshot result).
+ *   sums_out  [tokens][hidden] act_dtype: rows [row_begin, row_begin + row_count) receive
+ *             the reduced value cast to act_dtype (the page's slice: tokens/N rows per
+ *             rank, the first tokens%N ranks one more). Other arguments as in
+ *             arf_fused_epilogue.
+ */
+arf_status arf_reduce_rows(const void* partials, int32_t n_shards, int64_t tokens,
+                           int64_t row_begin, int64_t row_count, int32_t hidden,
+                           int32_t partial_dtype, int32_t act_dtype, int32_t accumulate,
+                           void* sums_out, void* stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* arf_status_string(int32_t status);

@@ -16,17 +16,32 @@ LIB_PATH = os.path.join(HERE, "libarfuse.so")
 
 ARF_BF16, ARF_F16, ARF_F32 = 0, 1, 2
 ARF_QUANT_PER_TENSOR, ARF_QUANT_PER_TOKEN = 0, 1
+ARF_ACC_F32, ARF_ACC_PARTIAL = 0, 1
 ARF_MAX_SHARDS, ARF_MAX_HIDDEN = 16, 65536
 STATUS = ["ARF_OK", "ARF_ERR_NULL", "ARF_ERR_SHAPE", "ARF_ERR_DTYPE", "ARF_ERR_ALIGN",
           "ARF_ERR_ALIAS", "ARF_ERR_NO_OUTPUT", "ARF_ERR_VALUE", "ARF_ERR_HIP"]
 
-# Exported symbols and their C signatures (kept in step with include/arfuse.h).
 _vp, _i32, _i64, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+
+
+class arf_params(ctypes.Structure):
+    """Mirror of ``arf_params`` in include/arfuse.h."""
+    _fields_ = [("struct_size", ctypes.c_uint32), ("n_shards", _i32), ("partials", _vp),
+                ("tokens", _i64), ("row_begin", _i64), ("row_count", _i64),
+                ("hidden", _i32), ("partial_dtype", _i32), ("act_dtype", _i32),
+                ("accumulate", _i32), ("residual_in", _vp), ("residual_out", _vp),
+                ("gamma", _vp), ("eps", _f32), ("norm_out", _vp), ("quant_out", _vp),
+                ("quant_mode", _i32), ("scale_in", _vp), ("scale_out", _vp)]
+
+
+# Exported symbols and their C signatures (kept in step with include/arfuse.h).
 SIGNATURES = {
     "arf_reduce_add_rmsnorm": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _f32,
                                       _vp, _vp]),
     "arf_reduce_add_rmsnorm_quant": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp,
                                             _f32, _vp, _vp, _i32, _vp, _vp, _vp]),
+    "arf_fused_epilogue": (_i32, [ctypes.POINTER(arf_params), _vp]),
+    "arf_reduce_rows": (_i32, [_vp, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp]),
     "arf_status_string": (ctypes.c_char_p, [_i32]),
     "arf_version": (_i32, []),
     "arf_get_plan": (_i32, [_i32, _i64, _i32, _i32, _i32, ctypes.POINTER(_i32)]),
@@ -116,6 +131,28 @@ def arf_reduce_add_rmsnorm_quant(partials, residual_in, gamma, eps: float, quant
         _ptr(residual_in), _ptr(residual_out), _ptr(gamma), float(eps), _ptr(norm_out),
         _ptr(quant_out), int(mode), _ptr(scale_in), _ptr(scale_out), _stream(stream))
     _check(st, "arf_reduce_add_rmsnorm_quant")
+
+
+def arf_fused_epilogue(partials, residual_in, gamma, eps: float, residual_out=None,
+                       norm_out=None, quant_out=None, mode: int = ARF_QUANT_PER_TOKEN,
+                       scale_in=None, scale_out=None, accumulate: int = ARF_ACC_F32,
+                       row_begin: int = 0, row_count: int = -1, stream=None) -> None:
+    """The general call: row range and accumulation mode (see arf_params)."""
+    n, t, h = partials.shape
+    a = arf_params(ctypes.sizeof(arf_params), n, _ptr(partials), t, row_begin, row_count, h,
+                   _dtype_code(partials), _dtype_code(residual_in), accumulate,
+                   _ptr(residual_in), _ptr(residual_out), _ptr(gamma), float(eps),
+                   _ptr(norm_out), _ptr(quant_out), mode, _ptr(scale_in), _ptr(scale_out))
+    _check(lib().arf_fused_epilogue(ctypes.byref(a), _stream(stream)), "arf_fused_epilogue")
+
+
+def arf_reduce_rows(partials, sums_out, row_begin: int = 0, row_count: int = -1,
+                    accumulate: int = ARF_ACC_F32, stream=None) -> None:
+    """Reduced values of rows [row_begin, row_begin + row_count) into sums_out [T][H]."""
+    n, t, h = partials.shape
+    _check(lib().arf_reduce_rows(_ptr(partials), n, t, row_begin, row_count, h,
+                                 _dtype_code(partials), _dtype_code(sums_out), accumulate,
+                                 _ptr(sums_out), _stream(stream)), "arf_reduce_rows")
 
 
 def arf_status_string(status: int) -> str:

@@ -48,18 +48,22 @@ enum QuantMode : int32_t { kQuantNone = 0, kQuantTensor = 1, kQuantToken = 2 };
 
 struct Params {
     const void* partials;
-    const void* residual_in;
-    void* residual_out;   // nullable
+    const void* residual_in;   // NULL in reduce-only mode (its loads then read nothing)
+    void* residual_out;        // nullable; the reduced values in reduce-only mode
     const void* gamma;
-    void* norm_out;       // nullable
-    uint8_t* quant_out;   // used when quant_mode != kQuantNone
+    void* norm_out;            // nullable
+    uint8_t* quant_out;        // used when quant_mode != kQuantNone
     const float* scale_in;
     float* scale_out;
-    int64_t tokens;
+    int64_t tokens;            // rows of every buffer (shard stride tokens * hidden)
+    int64_t row_begin;         // first row of this launch
+    int64_t row_end;           // one past the last row of this launch
     int32_t hidden;
     int32_t n_shards;
     float eps;
     int32_t quant_mode;
+    int32_t acc_partial;       // round every partial sum to the partial type
+    int32_t reduce_only;       // store the reduced value and stop
 };
 
 struct ActBF16 {};
@@ -241,11 +245,11 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
     int64_t row;
     int gl;
     if constexpr (ROW_PER_WAVE) {
-        row = (int64_t)blockIdx.x * WAVES + __builtin_amdgcn_readfirstlane(wave);
-        if (row >= p.tokens) return;   // whole wavefront leaves; no workgroup barrier here
+        row = p.row_begin + (int64_t)blockIdx.x * WAVES + __builtin_amdgcn_readfirstlane(wave);
+        if (row >= p.row_end) return;   // whole wavefront leaves; no workgroup barrier here
         gl = lane;
     } else {
-        row = blockIdx.x;
+        row = p.row_begin + (int64_t)blockIdx.x;
         gl = threadIdx.x;
     }
 
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
     const uint32_t part_row = H * (uint32_t)PartTraits<PT>::kBytes;
     const int64_t act_off = row * (int64_t)act_row;
 
-    const auto r_in = make_rsrc((const char*)p.residual_in + act_off, act_row);
+    const auto r_in = make_rsrc((const char*)p.residual_in + act_off, p.residual_in ? act_row : 0u);
     const auto r_out = make_rsrc((char*)p.residual_out + act_off, p.residual_out ? act_row : 0u);
     const auto y_out = make_rsrc((char*)p.norm_out + act_off, p.norm_out ? act_row : 0u);
     const auto g_in = make_rsrc(p.gamma, act_row);
@@ -295,9 +299,28 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
         for (int j = 0; j < C; ++j) {
             float t[8];
             load_partial_chunk(AT{}, buf[slot][j], t);
+            if (r == 0) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[j][e] = r == 0 ? t[e] : acc[j][e] + t[e];
+                for (int e = 0; e < 8; ++e) acc[j][e] = t[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[j][e] = acc[j][e] + t[e];
+                if constexpr (PW == 1) {
+                    // the other branch of the page's sum: each partial sum rounded to the
+                    // (16-bit) partial type; a select, so the load schedule is unchanged
+                    float rnd[8];
+                    unpack8(PT{}, pack8(PT{}, acc[j]), rnd);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[j][e] = p.acc_partial ? rnd[e] : acc[j][e];
+                }
+            }
         }
+    }
+
+    if (p.reduce_only) {   // one rank's share of the token-slice exchange
+#pragma unroll
+        for (int j = 0; j < C; ++j) L::store_act(pack8(AT{}, acc[j]), r_out, j, gl);
+        return;
     }
 
     // ---- cast, residual add, cast, store; sum of squares of the stored value

@@ -130,34 +130,48 @@ struct Call {
     const void* partials;
     int32_t n;
     int64_t tokens;
+    int64_t row_begin;
+    int64_t row_count;   // < 0: through the last row
     int32_t hidden;
     int32_t pdt, adt;
+    int32_t acc;         // ARF_ACC_*
     const void* residual_in;
-    void* residual_out;
+    void* residual_out;  // the reduced values in reduce-only mode
     const void* gamma;
     float eps;
     void* norm_out;
     uint8_t* quant_out;
-    int32_t quant;   // arf::QuantMode
+    int32_t quant;       // arf::QuantMode
     const float* scale_in;
     float* scale_out;
+    bool reduce_only;
 };
 
-// Order: sizes, types and eps first; an empty call (tokens == 0) is then complete, so
-// its pointers may be NULL (zero-size tensors often have no address); otherwise
-// pointers, alignment and overlaps.
-arf_status validate(const Call& c) {
+// Order: sizes, types, mode and eps first; then the row range. An empty range is then a
+// complete call, so its pointers may be NULL (zero-size tensors often have no address);
+// otherwise pointers, alignment and overlaps (over the buffers' full [tokens] extents).
+arf_status validate(Call& c) {
     if (c.n < 1 || c.n > ARF_MAX_SHARDS || c.tokens < 0 || c.tokens > INT32_MAX ||
         c.hidden <= 0 || c.hidden % 8 != 0 || c.hidden > ARF_MAX_HIDDEN)
         return ARF_ERR_SHAPE;
     if (c.adt != ARF_BF16 && c.adt != ARF_F16) return ARF_ERR_DTYPE;
     if (c.pdt != c.adt && c.pdt != ARF_F32) return ARF_ERR_DTYPE;
+    if (c.acc != ARF_ACC_F32 && c.acc != ARF_ACC_PARTIAL) return ARF_ERR_VALUE;
     if (!(c.eps >= 0.0f) || std::isinf(c.eps)) return ARF_ERR_VALUE;
-    if (c.tokens == 0) return ARF_OK;
-    if (!c.partials || !c.residual_in || !c.gamma) return ARF_ERR_NULL;
-    if (c.quant == arf::kQuantTensor && (!c.quant_out || !c.scale_in)) return ARF_ERR_NULL;
-    if (c.quant == arf::kQuantToken && (!c.quant_out || !c.scale_out)) return ARF_ERR_NULL;
-    if (c.quant == arf::kQuantNone && !c.residual_out && !c.norm_out) return ARF_ERR_NO_OUTPUT;
+    if (c.row_begin < 0 || c.row_begin > c.tokens) return ARF_ERR_SHAPE;
+    if (c.row_count < 0) c.row_count = c.tokens - c.row_begin;
+    if (c.row_count > c.tokens - c.row_begin) return ARF_ERR_SHAPE;
+    if (c.row_count == 0) return ARF_OK;
+    if (!c.partials) return ARF_ERR_NULL;
+    if (c.reduce_only) {
+        if (!c.residual_out) return ARF_ERR_NULL;
+    } else {
+        if (!c.residual_in || !c.gamma) return ARF_ERR_NULL;
+        if (c.quant == arf::kQuantTensor && (!c.quant_out || !c.scale_in)) return ARF_ERR_NULL;
+        if (c.quant == arf::kQuantToken && (!c.quant_out || !c.scale_out)) return ARF_ERR_NULL;
+        if (c.quant == arf::kQuantNone && !c.residual_out && !c.norm_out)
+            return ARF_ERR_NO_OUTPUT;
+    }
     const void* t16[] = {c.partials, c.residual_in, c.residual_out, c.gamma, c.norm_out,
                          c.quant_out};
     for (const void* p : t16)
@@ -169,8 +183,8 @@ arf_status validate(const Call& c) {
     const int64_t th = c.tokens * (int64_t)c.hidden;
     const int64_t sp = c.pdt == ARF_F32 ? 4 : 2;
     Range in_part = span(c.partials, (int64_t)c.n * th * sp);
-    Range in_res = span(c.residual_in, th * 2);
-    Range in_gam = span(c.gamma, (int64_t)c.hidden * 2);
+    Range in_res = c.residual_in ? span(c.residual_in, th * 2) : Range{0, 0};
+    Range in_gam = c.gamma ? span(c.gamma, (int64_t)c.hidden * 2) : Range{0, 0};
     Range in_sc = c.quant == arf::kQuantTensor ? span(c.scale_in, 4) : Range{0, 0};
     Range outs[4] = {
         c.residual_out ? span(c.residual_out, th * 2) : Range{0, 0},
@@ -190,29 +204,33 @@ arf_status validate(const Call& c) {
     return ARF_OK;
 }
 
-arf_status run(const Call& c, void* stream) {
+arf_status run(Call c, void* stream) {
     arf_status st = validate(c);
-    if (st != ARF_OK || c.tokens == 0) return st;
+    if (st != ARF_OK || c.row_count == 0) return st;
     int cus = 0;
     if ((st = device_cus(&cus)) != ARF_OK) return st;
     Plan pl;
-    if ((st = make_plan(c.tokens, c.hidden, cus, &pl)) != ARF_OK) return st;
+    if ((st = make_plan(c.row_count, c.hidden, cus, &pl)) != ARF_OK) return st;
     launch_fn fn = lookup(c.pdt, c.adt, c.n, pl);
     if (!fn) return ARF_ERR_VALUE;
     arf::Params p;
     p.partials = c.partials;
-    p.residual_in = c.residual_in;
+    p.residual_in = c.reduce_only ? nullptr : c.residual_in;
     p.residual_out = c.residual_out;
     p.gamma = c.gamma;
-    p.norm_out = c.norm_out;
+    p.norm_out = c.reduce_only ? nullptr : c.norm_out;
     p.quant_out = c.quant_out;
     p.scale_in = c.scale_in;
     p.scale_out = c.scale_out;
     p.tokens = c.tokens;
+    p.row_begin = c.row_begin;
+    p.row_end = c.row_begin + c.row_count;
     p.hidden = c.hidden;
     p.n_shards = c.n;
     p.eps = c.eps;
-    p.quant_mode = c.quant;
+    p.quant_mode = c.reduce_only ? arf::kQuantNone : c.quant;
+    p.acc_partial = c.acc == ARF_ACC_PARTIAL;
+    p.reduce_only = c.reduce_only;
     if (fn(p, pl.grid, (hipStream_t)stream) != hipSuccess) return ARF_ERR_HIP;
     return ARF_OK;
 }
@@ -268,8 +286,9 @@ arf_status arf_reduce_add_rmsnorm(const void* partials, int32_t n_shards, int64_
                                   const void* residual_in, void* residual_out,
                                   const void* gamma, float eps, void* norm_out,
                                   void* stream) {
-    Call c{partials, n_shards, tokens, hidden, partial_dtype, act_dtype, residual_in,
-           residual_out, gamma, eps, norm_out, nullptr, arf::kQuantNone, nullptr, nullptr};
+    Call c{partials, n_shards, tokens, 0, -1, hidden, partial_dtype, act_dtype, ARF_ACC_F32,
+           residual_in, residual_out, gamma, eps, norm_out, nullptr, arf::kQuantNone,
+           nullptr, nullptr, false};
     return run(c, stream);
 }
 
@@ -285,10 +304,37 @@ arf_status arf_reduce_add_rmsnorm_quant(const void* partials, int32_t n_shards,
     if (mode == ARF_QUANT_PER_TENSOR) q = arf::kQuantTensor;
     else if (mode == ARF_QUANT_PER_TOKEN) q = arf::kQuantToken;
     else return ARF_ERR_VALUE;
-    Call c{partials, n_shards, tokens, hidden, partial_dtype, act_dtype, residual_in,
-           residual_out, gamma, eps, norm_out, quant_out, q,
+    Call c{partials, n_shards, tokens, 0, -1, hidden, partial_dtype, act_dtype, ARF_ACC_F32,
+           residual_in, residual_out, gamma, eps, norm_out, quant_out, q,
            q == arf::kQuantTensor ? scale_in : nullptr,
-           q == arf::kQuantToken ? scale_out : nullptr};
+           q == arf::kQuantToken ? scale_out : nullptr, false};
+    return run(c, stream);
+}
+
+arf_status arf_fused_epilogue(const arf_params* a, void* stream) {
+    if (!a) return ARF_ERR_NULL;
+    if (a->struct_size != sizeof(arf_params)) return ARF_ERR_VALUE;
+    int32_t q = arf::kQuantNone;
+    if (a->quant_out) {
+        if (a->quant_mode == ARF_QUANT_PER_TENSOR) q = arf::kQuantTensor;
+        else if (a->quant_mode == ARF_QUANT_PER_TOKEN) q = arf::kQuantToken;
+        else return ARF_ERR_VALUE;
+    }
+    Call c{a->partials, a->n_shards, a->tokens, a->row_begin, a->row_count, a->hidden,
+           a->partial_dtype, a->act_dtype, a->accumulate, a->residual_in, a->residual_out,
+           a->gamma, a->eps, a->norm_out, q != arf::kQuantNone ? a->quant_out : nullptr, q,
+           q == arf::kQuantTensor ? a->scale_in : nullptr,
+           q == arf::kQuantToken ? a->scale_out : nullptr, false};
+    return run(c, stream);
+}
+
+arf_status arf_reduce_rows(const void* partials, int32_t n_shards, int64_t tokens,
+                           int64_t row_begin, int64_t row_count, int32_t hidden,
+                           int32_t partial_dtype, int32_t act_dtype, int32_t accumulate,
+                           void* sums_out, void* stream) {
+    Call c{partials, n_shards, tokens, row_begin, row_count, hidden, partial_dtype,
+           act_dtype, accumulate, nullptr, sums_out, nullptr, 0.0f, nullptr, nullptr,
+           arf::kQuantNone, nullptr, nullptr, true};
     return run(c, stream);
 }
 

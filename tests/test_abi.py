@@ -27,14 +27,14 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     L = arf.lib()
     names = declared_symbols()
-    assert len(names) == 8
+    assert len(names) == 10
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(arf.SIGNATURES)
 
 
 def test_version_and_status_strings():
-    assert arf.arf_version() == 100
+    assert arf.arf_version() == 200
     for code, name in enumerate(arf.STATUS):
         assert arf.arf_status_string(code).startswith(name)
     assert "unknown" in arf.arf_status_string(99)
@@ -167,3 +167,46 @@ def test_no_device_returns_hip_error():
         pytest.skip("a GPU is present: this case would launch on fake addresses")
     assert call() == HIP
     assert arf.lib().arf_stream_copy(Q, P, 64, None) == HIP
+
+
+def params(**kw):
+    a = dict(n=2, partials=P, tokens=4, row_begin=0, row_count=-1, hidden=64, pdt=0, adt=0,
+             acc=0, rin=R, rout=RO, gamma=G, eps=1e-6, nout=NO, q=None, mode=1, sin=None,
+             sout=None, size=ctypes.sizeof(arf.arf_params))
+    a.update(kw)
+    return arf.arf_params(a["size"], a["n"], a["partials"], a["tokens"], a["row_begin"],
+                          a["row_count"], a["hidden"], a["pdt"], a["adt"], a["acc"], a["rin"],
+                          a["rout"], a["gamma"], a["eps"], a["nout"], a["q"], a["mode"],
+                          a["sin"], a["sout"])
+
+
+def callp(**kw):
+    return arf.lib().arf_fused_epilogue(ctypes.byref(params(**kw)), None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(size=8), VALUE), (dict(acc=2), VALUE), (dict(acc=-1), VALUE),
+    (dict(row_begin=-1), SHAPE), (dict(row_begin=5), SHAPE), (dict(row_begin=2, row_count=3), SHAPE),
+    (dict(row_begin=4, row_count=0), OK), (dict(row_begin=4), OK), (dict(row_begin=1, row_count=0), OK),
+    (dict(partials=None), NULL), (dict(rout=None, nout=None), NOOUT),
+    (dict(q=Q, mode=1, sout=None), NULL), (dict(q=Q, mode=3), VALUE), (dict(q=Q, mode=0, sin=None), NULL),
+    (dict(q=Q + 8, mode=1, sout=S), ALIGN), (dict(nout=R), ALIAS),
+    (dict(tokens=0), OK), (dict(n=0), SHAPE), (dict(adt=2), DTYPE),
+])
+def test_general_entry_point_validation(kw, want):
+    assert callp(**kw) == want
+
+
+def test_null_params_and_reduce_rows_validation():
+    L = arf.lib()
+    assert L.arf_fused_epilogue(None, None) == NULL
+    rr = L.arf_reduce_rows
+    assert rr(P, 2, 4, 0, -1, 64, 0, 0, 0, None, None) == NULL
+    assert rr(None, 2, 4, 0, -1, 64, 0, 0, 0, RO, None) == NULL
+    assert rr(P, 2, 4, 0, -1, 64, 0, 0, 0, P + 64, None) == ALIAS
+    assert rr(P, 2, 4, 3, 2, 64, 0, 0, 0, RO, None) == SHAPE
+    assert rr(P, 2, 4, 0, -1, 64, 0, 0, 5, RO, None) == VALUE
+    assert rr(P, 2, 4, 0, -1, 64, 1, 0, 0, RO, None) == DTYPE
+    assert rr(P, 2, 4, 0, -1, 64, 0, 0, 0, RO + 4, None) == ALIGN
+    assert rr(P, 2, 4, 4, -1, 64, 0, 0, 0, None, None) == OK      # empty range
+    assert rr(P, 2, 0, 0, -1, 64, 0, 0, 0, None, None) == OK

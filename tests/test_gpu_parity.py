@@ -358,3 +358,95 @@ def test_stream_copy_is_exact():
         torch.cuda.synchronize()
         assert torch.equal(dst[:nbytes], src)
         assert bool((dst[nbytes:] == CANARY).all())
+
+
+# ---- accumulation in the partial type, row ranges, reduce-only ----------------------------
+
+@pytest.mark.parametrize("pd,ad", [("bf16", "bf16"), ("f16", "f16"), ("f32", "bf16")])
+@pytest.mark.parametrize("n", [2, 3, 8, 16])
+def test_partial_accumulation_parity(pd, ad, n):
+    w = _case(n, 9, 2056, pd, ad, 500 + n, quant="per_token", std=4.0)
+    say("partial accumulation n=%d %s/%s" % (n, pd, ad))
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    ref = run_oracle(p, r, g, w.eps, pd, ad, quant="per_token", accumulate="partial")
+    t, h = r.shape
+    rout, nout = Out((t, h), TORCH[ad]), Out((t, h), TORCH[ad])
+    q, sc = Out((t, h), torch.uint8), Out((t,), torch.float32)
+    arf.arf_fused_epilogue(pd_, rd, gd, w.eps, residual_out=rout.t, norm_out=nout.t,
+                           quant_out=q.t, scale_out=sc.t, accumulate=arf.ARF_ACC_PARTIAL)
+    torch.cuda.synchronize()
+    assert all(o.canary_ok() for o in (rout, nout, q, sc))
+    got = {"residual_out": workloads.to_bits(rout.t), "norm_out": workloads.to_bits(nout.t),
+           "quant_out": q.t.cpu().numpy(), "scale_out": sc.t.cpu().numpy()}
+    compare(got, ref, "partial acc n=%d" % n)
+    if pd != "f32" and n >= 8:   # the two branches really differ here
+        ref32 = run_oracle(p, r, g, w.eps, pd, ad)
+        assert not np.array_equal(ref32["residual_out"], ref["residual_out"])
+
+
+def test_partial_accumulation_golden_on_gpu():
+    from helpers import read_golden, exact_to_act_bits, act_bits_to_f64
+    for act, acc, *vals in read_golden("partial_accumulation.txt"):
+        say("golden partial accumulation %s %s %s" % (act, acc, vals))
+        h = 64
+        pv = torch.tensor([float(v) for v in vals[:4]], dtype=torch.float64)
+        p = pv[:, None, None].expand(4, 2, h).contiguous().to(TORCH[act]).to(DEV)
+        zero = torch.zeros((2, h), dtype=TORCH[act], device=DEV)
+        g = torch.ones((h,), dtype=TORCH[act], device=DEV)
+        out = torch.empty((2, h), dtype=TORCH[act], device=DEV)
+        arf.arf_fused_epilogue(p, zero, g, 1e-6, residual_out=out,
+                               accumulate=arf.ARF_ACC_PARTIAL if acc == "partial" else arf.ARF_ACC_F32)
+        sums = torch.empty((2, h), dtype=TORCH[act], device=DEV)
+        arf.arf_reduce_rows(p, sums, accumulate=arf.ARF_ACC_PARTIAL if acc == "partial" else arf.ARF_ACC_F32)
+        torch.cuda.synchronize()
+        assert torch.all(out.double() == float(vals[4])) and torch.all(sums.double() == float(vals[4]))
+
+
+@pytest.mark.parametrize("begin,count", [(0, 7), (5, 11), (13, -1), (40, 1), (0, -1), (20, 0)])
+def test_row_ranges(begin, count):
+    w = _case(8, 41, 4096, "bf16", "bf16", 600, quant="per_token")
+    say("row range %d %d" % (begin, count))
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    ref = run_oracle(p, r, g, w.eps, "bf16", "bf16", quant="per_token", rows=(begin, count),
+                     out_init=POISON)
+    t, h = r.shape
+    rout, nout = Out((t, h), torch.bfloat16), Out((t, h), torch.bfloat16)
+    q, sc = Out((t, h), torch.uint8), Out((t,), torch.float32)
+    arf.arf_fused_epilogue(pd_, rd, gd, w.eps, residual_out=rout.t, norm_out=nout.t,
+                           quant_out=q.t, scale_out=sc.t, row_begin=begin, row_count=count)
+    torch.cuda.synchronize()
+    assert all(o.canary_ok() for o in (rout, nout, q, sc))
+    end = t if count < 0 else begin + count
+    got = {"residual_out": workloads.to_bits(rout.t), "norm_out": workloads.to_bits(nout.t),
+           "quant_out": q.t.cpu().numpy(), "scale_out": sc.t.cpu().numpy()}
+    for k in got:   # rows outside the range were never written (still the poison bytes)
+        outside = np.concatenate([got[k][:begin].ravel().view(np.uint8),
+                                  got[k][end:].ravel().view(np.uint8)])
+        assert np.all(outside == POISON), k
+    inside = {k: v[begin:end] for k, v in got.items()}
+    want = {k: v[begin:end] for k, v in ref.items()}
+    if end > begin:
+        compare(inside, want, "rows %d..%d" % (begin, end))
+
+
+@pytest.mark.parametrize("pd,ad", [("bf16", "bf16"), ("f32", "f16")])
+def test_reduce_rows_and_twoshot_composition(pd, ad):
+    n, t, h = 8, 37, 7168
+    w = _case(n, t, h, pd, ad, 700, quant="per_token")
+    say("reduce rows / twoshot %s/%s" % (pd, ad))
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    gathered = Out((t, h), TORCH[ad])
+    for rank in range(n):   # the page's launcher: t // n rows each, the first t % n one more
+        cnt = t // n + (1 if rank < t % n else 0)
+        beg = rank * (t // n) + min(rank, t % n)
+        arf.arf_reduce_rows(pd_, gathered.t, row_begin=beg, row_count=cnt)
+    torch.cuda.synchronize()
+    assert gathered.canary_ok()
+    sums = oracle.reduce_rows(workloads.to_bits(p), partial_dtype=pd, act_dtype=ad)
+    assert np.array_equal(workloads.to_bits(gathered.t), sums)
+    # epilogue over the gathered values with one "shard" == the oneshot result
+    two = run_gpu(gathered.t.view(1, t, h), rd, gd, w.eps, ad, quant="per_token")
+    one = run_gpu(pd_, rd, gd, w.eps, ad, quant="per_token")
+    for k in one:
+        assert np.array_equal(two[k], one[k]), k
+    compare(one, run_oracle(p, r, g, w.eps, pd, ad, quant="per_token"), "oneshot")
