@@ -12,7 +12,7 @@ patterns; fp32 partials as ``np.float32``.
 Method: TensorRT-LLM page "allReduceFusionKernels.cu" (allreduce_sum, add128,
 rms_norm, fused_op, oneshot-sync post-barrier loop); FlashInfer page for
 trtllm_create_ipc_workspace_for_all_reduce_fusion (buffer shape, fp32 partials);
-OCP OFP8 rev 1.0 (E4M3).
+OCP OFP8 rev 1.0 (E4M3); OCP Microscaling Formats v1.0 (MXFP4).
 """
 from __future__ import annotations
 
@@ -27,7 +27,7 @@ _SRC = os.path.join(_HERE, "arf_oracle.c")
 _LIB = os.path.join(_HERE, "libarf_oracle.so")
 
 DTYPES = {"bf16": 0, "f16": 1, "f32": 2}
-MODES = {"per_tensor": 0, "per_token": 1}
+MODES = {"per_tensor": 0, "per_token": 1, "mxfp4": 2}
 ACCUMULATE = {"f32": 0, "partial": 1}
 
 
@@ -78,6 +78,12 @@ def lib() -> ctypes.CDLL:
         L.arfo_f16_to_f32.restype = f32
         L.arfo_e4m3_to_f32.argtypes = [ctypes.c_uint8]
         L.arfo_e4m3_to_f32.restype = f32
+        L.arfo_f32_to_e2m1.argtypes = [f32]
+        L.arfo_f32_to_e2m1.restype = ctypes.c_uint8
+        L.arfo_e2m1_to_f32.argtypes = [ctypes.c_uint8]
+        L.arfo_e2m1_to_f32.restype = f32
+        L.arfo_mx_scale_code.argtypes = [f32]
+        L.arfo_mx_scale_code.restype = ctypes.c_uint8
         for name in ("arfo_f32_to_bf16_n", "arfo_f32_to_f16_n", "arfo_f32_to_e4m3_n"):
             getattr(L, name).argtypes = [vp, vp, i64]
             getattr(L, name).restype = None
@@ -129,6 +135,18 @@ def f32_to_e4m3(x) -> np.ndarray:
     return out
 
 
+def f32_to_e2m1(x) -> np.ndarray:
+    f = lib().arfo_f32_to_e2m1
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return np.array([f(float(v)) for v in x.ravel()], np.uint8).reshape(x.shape)
+
+
+def mx_scale_code(amax) -> np.ndarray:
+    f = lib().arfo_mx_scale_code
+    a = np.ascontiguousarray(amax, dtype=np.float32)
+    return np.array([f(float(v)) for v in a.ravel()], np.uint8).reshape(a.shape)
+
+
 def bf16_to_f32(b) -> np.ndarray:
     b = np.ascontiguousarray(b, dtype=np.uint16)
     return (b.astype(np.uint32) << 16).view(np.float32)
@@ -168,7 +186,9 @@ def reduce_add_rmsnorm(partials: np.ndarray, residual_in: np.ndarray, gamma: np.
     ``residual_in`` [T][H] uint16 bits, ``gamma`` [H] uint16 bits.
 
     Returns a dict with ``residual_out`` / ``norm_out`` (uint16 bits), ``quant_out``
-    (uint8 codes) and ``scale_out`` (float32 [T], per-token mode) as requested.
+    (uint8 codes; "mxfp4": [T][H/2], two E2M1 codes per byte, even element in the low
+    nibble) and ``scale_out`` (float32 [T] for "per_token"; uint8 E8M0 [T][H/32] for
+    "mxfp4") as requested.
     ``residual_out_array`` may be ``residual_in`` itself to run in place. ``accumulate``
     is "f32" (the default branch) or "partial" (rounded to the partial type after every
     addition). ``rows`` = (begin, count) restricts the computed rows; output rows outside
@@ -204,12 +224,17 @@ def reduce_add_rmsnorm(partials: np.ndarray, residual_in: np.ndarray, gamma: np.
     mode = -1
     if quant is not None:
         mode = MODES[quant]
-        q = new((t, h), np.uint8)
+        if quant == "mxfp4":
+            q = new((t, h // 2), np.uint8)
+            sout = new((t, h // 32), np.uint8)
+        else:
+            q = new((t, h), np.uint8)
         out["quant_out"] = q
         if quant == "per_tensor":
             sin = np.array([scale_in], np.float32)
-        else:
+        elif quant == "per_token":
             sout = new((t,), np.float32)
+        if sout is not None:
             out["scale_out"] = sout
     begin, count = (0, -1) if rows is None else rows
     a = Args(_ptr(partials), n, t, h, DTYPES[partial_dtype], DTYPES[act_dtype],

@@ -22,6 +22,9 @@
  *           trtllm_create_ipc_workspace_for_all_reduce_fusion (tp_size x tokens x hidden
  *           buffers; 4-byte elements with use_fp32_lamport).
  *   [OFP8]  OCP 8-bit Floating Point Specification (OFP8) rev 1.0, E4M3 encoding.
+ *   [MX]    OCP Microscaling Formats (MX) v1.0: MXFP4 = blocks of 32 FP4 (E2M1) elements
+ *           sharing one E8M0 scale X = 2^(floor(log2(max |V|)) - emax_elem), emax_elem = 2,
+ *           elements quantised from V / X (round to nearest even, saturating).
  */
 #include "arf_oracle.h"
 
@@ -148,6 +151,44 @@ float arfo_e4m3_to_f32(uint8_t q)
     return (float)(sign ? -v : v);
 }
 
+/* OCP MX FP4 E2M1 [MX]: 2 exponent bits (bias 1), 1 mantissa bit, emin = 0, largest
+   finite 1.5 * 2^2 = 6, smallest subnormal 0.5, no infinities or NaN. Round to nearest even,
+   saturating to +-6 (infinities too; NaN is not produced by the method and maps to +-6). */
+uint8_t arfo_f32_to_e2m1(float x)
+{
+    uint8_t sign = (uint8_t)((f32_bits(x) >> 28) & 0x8u);
+    if (isnan(x) || isinf(x)) return (uint8_t)(sign | 0x7u);
+    double r = fabs(round_to_format((double)x, 1, 0));
+    if (r > 6.0) r = 6.0;
+    if (r == 0.0) return sign;
+    int e;
+    (void)frexp(r, &e);
+    int ex = e - 1;
+    if (ex < 0) return (uint8_t)(sign | 0x1u);            /* subnormal: 0.5 */
+    uint8_t m = (uint8_t)(ldexp(r, -ex) * 2.0 - 2.0);
+    return (uint8_t)(sign | (uint8_t)((ex + 1) << 1) | m);
+}
+
+float arfo_e2m1_to_f32(uint8_t q)
+{
+    int sign = (q >> 3) & 1;
+    int ef = (q >> 1) & 0x3;
+    int m = q & 0x1;
+    double v = ef == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, ef - 1);
+    return (float)(sign ? -v : v);
+}
+
+uint8_t arfo_mx_scale_code(float amax)
+{
+    if (!(amax > 0.0f)) return 0;
+    int e;
+    (void)frexp((double)amax, &e);
+    int shared = (e - 1) - 2;                             /* floor(log2 amax) - emax_elem */
+    if (shared < -127) shared = -127;
+    if (shared > 127) shared = 127;
+    return (uint8_t)(shared + 127);
+}
+
 void arfo_f32_to_bf16_n(const float* x, uint16_t* out, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = arfo_f32_to_bf16(x[i]);
@@ -198,10 +239,10 @@ typedef struct {
     const uint16_t* gamma;
     float eps;
     uint16_t* norm_out;
-    uint8_t* quant_out;       /* NULL when no fp8 copy is asked for */
+    uint8_t* quant_out;       /* NULL when no quantised copy is asked for */
     int32_t mode;
     const float* scale_in;
-    float* scale_out;
+    void* scale_out;
 } job_t;
 
 /* Round an fp32 value to the partial type (identity for fp32 partials). */
@@ -271,6 +312,29 @@ static void one_token(const job_t* j, int64_t t, uint16_t* rrow, uint16_t* yrow)
     if (j->norm_out)
         for (int64_t i = 0; i < H; ++i) j->norm_out[row + i] = yrow[i];
 
+    /* O6': MXFP4 copy of the cast normalised output [MX]: per block of 32 elements,
+       X = 2^(floor(log2 max|y|) - 2) (E8M0), codes E2M1(y / X); y / X is a power-of-two
+       scaling, exact in fp64. */
+    if (j->quant_out && j->mode == ARFO_MXFP4) {
+        uint8_t* qrow = j->quant_out + t * (H / 2);
+        uint8_t* srow = (uint8_t*)j->scale_out + t * (H / 32);
+        for (int64_t b = 0; b < H / 32; ++b) {
+            float amax = 0.0f;
+            for (int64_t i = 32 * b; i < 32 * b + 32; ++i) {
+                float a = fabsf(act_to_f32(yrow[i], j->adt));
+                if (a > amax) amax = a;
+            }
+            uint8_t code = arfo_mx_scale_code(amax);
+            srow[b] = code;
+            double inv_x = ldexp(1.0, 127 - (int)code);       /* 1 / 2^(code - 127) */
+            for (int64_t i = 32 * b; i < 32 * b + 32; i += 2) {
+                uint8_t lo = arfo_f32_to_e2m1((float)((double)act_to_f32(yrow[i], j->adt) * inv_x));
+                uint8_t hi = arfo_f32_to_e2m1((float)((double)act_to_f32(yrow[i + 1], j->adt) * inv_x));
+                qrow[i / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+        return;
+    }
     /* O6: fp8-e4m3 copy of the cast normalised output, v = y * (1/scale). */
     if (j->quant_out) {
         float scale;
@@ -281,7 +345,7 @@ static void one_token(const job_t* j, int64_t t, uint16_t* rrow, uint16_t* yrow)
                 if (a > amax) amax = a;
             }
             scale = amax / 448.0f;
-            j->scale_out[t] = scale;
+            ((float*)j->scale_out)[t] = scale;
         } else {
             scale = j->scale_in[0];
         }
@@ -382,6 +446,9 @@ int arfo_run(const arfo_args* a)
             if (!a->scale_in) return ARFO_ERR_NULL;
         } else if (a->quant_mode == ARFO_PER_TOKEN) {
             if (!a->scale_out) return ARFO_ERR_NULL;
+        } else if (a->quant_mode == ARFO_MXFP4) {
+            if (!a->scale_out) return ARFO_ERR_NULL;
+            if (a->hidden % 32 != 0) return ARFO_ERR_SHAPE;
         } else {
             return ARFO_ERR_VALUE;
         }

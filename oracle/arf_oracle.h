@@ -29,8 +29,9 @@ enum { ARFO_BF16 = 0, ARFO_F16 = 1, ARFO_F32 = 2 };
 /* Accumulation of the shards: fp32 (the page's default), or in the partial type with a
    rounding after every addition (the page's other branch, add128 in DType). */
 enum { ARFO_ACC_F32 = 0, ARFO_ACC_PARTIAL = 1 };
-/* fp8 scale modes. */
-enum { ARFO_PER_TENSOR = 0, ARFO_PER_TOKEN = 1 };
+/* Quantised-copy modes: fp8-e4m3 with a per-tensor or per-token scale; OCP MXFP4 (E2M1
+   elements in blocks of 32 sharing an E8M0 scale). */
+enum { ARFO_PER_TENSOR = 0, ARFO_PER_TOKEN = 1, ARFO_MXFP4 = 2 };
 /* Error codes. */
 enum { ARFO_OK = 0, ARFO_ERR_NULL = 1, ARFO_ERR_SHAPE = 2, ARFO_ERR_DTYPE = 3, ARFO_ERR_VALUE = 4 };
 
@@ -41,6 +42,11 @@ uint16_t arfo_f32_to_f16(float x);    /* overflow -> +-inf, NaN -> quiet NaN    
 float    arfo_f16_to_f32(uint16_t h);
 uint8_t  arfo_f32_to_e4m3(float x);   /* OCP E4M3, saturating to +-448, NaN -> S.1111.111 */
 float    arfo_e4m3_to_f32(uint8_t q);
+uint8_t  arfo_f32_to_e2m1(float x);   /* OCP MX FP4 E2M1 code (4 bits), saturating to +-6 */
+float    arfo_e2m1_to_f32(uint8_t q);
+/* OCP MX block scale of a block whose largest magnitude is amax (finite, >= 0): the
+   E8M0 code 127 + clamp(floor(log2 amax) - 2, -127, 127); 0 for amax == 0. */
+uint8_t  arfo_mx_scale_code(float amax);
 
 /* Bulk conversions (n elements), for tests. */
 void arfo_f32_to_bf16_n(const float* x, uint16_t* out, int64_t n);
@@ -77,7 +83,7 @@ int arfo_reduce_add_rmsnorm_quant(const void* partials, int32_t n_shards, int64_
 /*
  * General form. Rows [row_begin, row_begin + row_count) of the [tokens] rows are computed
  * (row_count < 0: to the end); every buffer keeps its full [tokens] layout and rows outside
- * the range are neither read nor written. quant_mode < 0: no fp8 copy.
+ * the range are neither read nor written. quant_mode < 0: no quantised copy.
  */
 typedef struct arfo_args {
     const void* partials;
@@ -94,10 +100,10 @@ typedef struct arfo_args {
     const void* gamma;
     float eps;
     void* norm_out;
-    uint8_t* quant_out;
+    uint8_t* quant_out;        /* MXFP4: [tokens][hidden/2], element 2k in the low nibble */
     int32_t quant_mode;
     const float* scale_in;
-    float* scale_out;
+    void* scale_out;           /* per-token: float [tokens]; MXFP4: uint8 [tokens][hidden/32] */
     int32_t n_threads;
 } arfo_args;
 

@@ -128,3 +128,35 @@ def e4m3_code_to_f64(q):
     mag = _E4M3[np.minimum(q & 0x7F, 0x7E)]
     mag = np.where((q & 0x7F) == 0x7F, np.nan, mag)
     return np.where(q & 0x80, -mag, mag)
+
+
+# ---- OCP MX FP4 (E2M1) by brute force ------------------------------------------------------
+
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])   # codes 0..7 (MX v1.0 table)
+
+
+def e2m1_brute(x):
+    """Nearest E2M1 magnitude, ties to the even code, saturating at 6; sign in bit 3."""
+    x = np.asarray(x, dtype=np.float64).ravel()
+    a = np.minimum(np.abs(x), 64.0)
+    d = np.abs(a[:, None] - _E2M1[None, :])
+    dmin = d.min(axis=1, keepdims=True)
+    cand = d == dmin
+    even = cand & ((np.arange(8) & 1) == 0)[None, :]
+    pick = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1)).astype(np.uint8)
+    return np.where(np.signbit(x), pick | 0x8, pick).astype(np.uint8)
+
+
+def e2m1_code_to_f64(q):
+    q = np.asarray(q, dtype=np.uint8)
+    mag = _E2M1[q & 0x7]
+    return np.where(q & 0x8, -mag, mag)
+
+
+def unpack_fp4(packed):
+    """[..., H/2] bytes -> [..., H] codes (element 2k in the low nibble)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
