@@ -56,9 +56,11 @@ extern "C" {
 #define ARF_ACC_F32 0
 #define ARF_ACC_PARTIAL 1
 
-/* fp8 scale modes. */
-#define ARF_QUANT_PER_TENSOR 0 /* y ~ code * scale_in[0], scale given by the caller */
-#define ARF_QUANT_PER_TOKEN 1  /* scale_out[t] = max_i |y[t][i]| / 448, written     */
+/* Quantised-copy modes. */
+#define ARF_QUANT_PER_TENSOR 0 /* fp8-e4m3, y ~ code * scale_in[0], scale given by the caller */
+#define ARF_QUANT_PER_TOKEN 1  /* fp8-e4m3, scale_out[t] = max_i |y[t][i]| / 448, written    */
+#define ARF_QUANT_MXFP4 2      /* OCP MXFP4 (arf_fused_epilogue only): blocks of 32 E2M1
+                                  codes sharing an E8M0 scale, see arf_params              */
 
 /* Limits. */
 #define ARF_MAX_SHARDS 16
@@ -132,7 +134,14 @@ arf_status arf_reduce_add_rmsnorm_quant(const void* partials, int32_t n_shards,
  *                neither read nor written. 0 <= row_begin <= tokens.
  *   accumulate   ARF_ACC_F32 or ARF_ACC_PARTIAL.
  *   quant_out    NULL for no quantised copy; else quant_mode, scale_in and scale_out as
- *                in arf_reduce_add_rmsnorm_quant.
+ *                in arf_reduce_add_rmsnorm_quant, or quant_mode ARF_QUANT_MXFP4 (OCP
+ *                Microscaling Formats v1.0, the 4-bit format that the page's quantised
+ *                output stands for here): hidden must be a multiple of 32;
+ *                quant_out [tokens][hidden/2] bytes, two E2M1 codes each (element 2k in
+ *                the low nibble, 16-byte aligned); scale_out [tokens][hidden/32] uint8
+ *                E8M0 codes, X = 2^(code - 127) = 2^(floor(log2 max|y|) - 2) per block of
+ *                32 (code 0 for an all-zero block); codes = E2M1(y / X), round to nearest
+ *                even, saturating at +-6.
  */
 typedef struct arf_params {
     uint32_t struct_size;
@@ -153,7 +162,7 @@ typedef struct arf_params {
     uint8_t* quant_out;
     int32_t quant_mode;
     const float* scale_in;
-    float* scale_out;
+    void* scale_out;
 } arf_params;
 
 arf_status arf_fused_epilogue(const arf_params* params, void* stream);

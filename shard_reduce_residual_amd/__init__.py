@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libarfuse.so")
 
 ARF_BF16, ARF_F16, ARF_F32 = 0, 1, 2
-ARF_QUANT_PER_TENSOR, ARF_QUANT_PER_TOKEN = 0, 1
+ARF_QUANT_PER_TENSOR, ARF_QUANT_PER_TOKEN, ARF_QUANT_MXFP4 = 0, 1, 2
 ARF_ACC_F32, ARF_ACC_PARTIAL = 0, 1
 ARF_MAX_SHARDS, ARF_MAX_HIDDEN = 16, 65536
 STATUS = ["ARF_OK", "ARF_ERR_NULL", "ARF_ERR_SHAPE", "ARF_ERR_DTYPE", "ARF_ERR_ALIGN",

@@ -44,7 +44,7 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kAuxStream = 2;
 constexpr int kAuxDefault = 0;
 
-enum QuantMode : int32_t { kQuantNone = 0, kQuantTensor = 1, kQuantToken = 2 };
+enum QuantMode : int32_t { kQuantNone = 0, kQuantTensor = 1, kQuantToken = 2, kQuantMx = 3 };
 
 struct Params {
     const void* partials;
@@ -54,7 +54,7 @@ struct Params {
     void* norm_out;            // nullable
     uint8_t* quant_out;        // used when quant_mode != kQuantNone
     const float* scale_in;
-    float* scale_out;
+    void* scale_out;           // float [tokens] (per token) or E8M0 bytes [tokens][hidden/32]
     int64_t tokens;            // rows of every buffer (shard stride tokens * hidden)
     int64_t row_begin;         // first row of this launch
     int64_t row_end;           // one past the last row of this launch
@@ -129,6 +129,28 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(a), e4m3_sat(b), 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(c), e4m3_sat(d), w, true);
     return (uint32_t)w;
+}
+
+// ---- OCP MX FP4 ------------------------------------------------------------------------------
+// E8M0 code of a block whose largest magnitude is amax (finite, >= 0): 127 + clamp(
+// floor(log2 amax) - 2, -127, 127), 0 for a zero block. frexp's exponent e has
+// amax = m * 2^e with m in [0.5, 1), so floor(log2 amax) = e - 1 (denormals included).
+__device__ __forceinline__ uint32_t mx_scale_code(float amax) {
+    if (!(amax > 0.0f)) return 0u;
+    int shared = __builtin_amdgcn_frexp_expf(amax) - 1 - 2;
+    shared = shared < -127 ? -127 : (shared > 127 ? 127 : shared);
+    return (uint32_t)(shared + 127);
+}
+
+// E2M1 code of v: round to nearest even over {0, 0.5, 1, 1.5, 2, 3, 4, 6}, saturating at 6.
+// Each comparison is a decision boundary; a tie goes to the even code (0.25 -> 0,
+// 0.75 -> 1.0, 1.25 -> 1.0, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4). Sign in bit 3.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+    const float a = __builtin_fabsf(v);
+    uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                 (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                 (uint32_t)(a > 5.0f);
+    return c | ((__builtin_bit_cast(uint32_t, v) >> 28) & 0x8u);
 }
 
 // ---- cross-lane reductions (wave64) ------------------------------------------------------
@@ -216,6 +238,49 @@ struct Layout {
         } else {
             __builtin_amdgcn_raw_buffer_store_b128(v, r, (uint32_t)(j * G + gl) * 16u, 0,
                                                    kAuxStream);
+        }
+    }
+    // MXFP4 codes and block scales of chunk j. In the 16-bit layout a 32-element block
+    // is 4 consecutive lanes (8 elements each); in the split layout it is 8 consecutive
+    // lanes' quads of the same half w. y: the lane's 8 cast outputs.
+    __device__ static void store_mx(const float y[8], __amdgpu_buffer_rsrc_t q,
+                                    __amdgpu_buffer_rsrc_t sc, int j, int gl) {
+        if constexpr (SPLIT) {
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+                float a = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a = fmaxf(a, __builtin_fabsf(y[4 * w + e]));
+                a = fmaxf(a, __shfl_xor(a, 1, 64));
+                a = fmaxf(a, __shfl_xor(a, 2, 64));
+                a = fmaxf(a, __shfl_xor(a, 4, 64));
+                const uint32_t code = mx_scale_code(a);
+                const float inv = __builtin_amdgcn_ldexpf(1.0f, 127 - (int)code);
+                uint32_t packed = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) packed |= e2m1_code(y[4 * w + e] * inv) << (4 * e);
+                const uint32_t u = (uint32_t)((2 * j + w) * G + gl);
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)packed, q, u * 2u, 0,
+                                                      kAuxStream);
+                if ((gl & 7) == 0)
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, sc, u / 8u, 0,
+                                                         kAuxStream);
+            }
+        } else {
+            float a = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = fmaxf(a, __builtin_fabsf(y[e]));
+            a = fmaxf(a, __shfl_xor(a, 1, 64));
+            a = fmaxf(a, __shfl_xor(a, 2, 64));
+            const uint32_t code = mx_scale_code(a);
+            const float inv = __builtin_amdgcn_ldexpf(1.0f, 127 - (int)code);
+            uint32_t packed = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) packed |= e2m1_code(y[e] * inv) << (4 * e);
+            const uint32_t c = (uint32_t)(j * G + gl);
+            __builtin_amdgcn_raw_buffer_store_b32(packed, q, c * 4u, 0, kAuxStream);
+            if ((gl & 3) == 0)
+                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, sc, c / 4u, 0, kAuxStream);
         }
     }
     // 8 fp8 codes of chunk j (q[0]: the first four elements, q[1]: the last four)
@@ -382,6 +447,19 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
     }
     if (p.quant_mode == kQuantNone) return;
 
+    // ---- MXFP4 copy: blocks of 32 share 2^(floor(log2 amax) - 2); E2M1 codes of y / X
+    if (p.quant_mode == kQuantMx) {
+        const auto q_mx = make_rsrc(p.quant_out + row * (int64_t)(H / 2), H / 2);
+        const auto s_mx = make_rsrc((uint8_t*)p.scale_out + row * (int64_t)(H / 32), H / 32);
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+            float y[8];
+            unpack8(AT{}, xr[j], y);
+            L::store_mx(y, q_mx, s_mx, j, gl);
+        }
+        return;
+    }
+
     // ---- fp8 copy: q = E4M3(y * (1/scale))
     float scale;
     if (p.quant_mode == kQuantToken) {
@@ -395,7 +473,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
             for (int w = 0; w < WAVES; ++w) amax = fmaxf(amax, s_max[w]);
         }
         scale = amax / 448.0f;
-        if (gl == 0) p.scale_out[row] = scale;
+        if (gl == 0) static_cast<float*>(p.scale_out)[row] = scale;
     } else {
         scale = p.scale_in[0];
     }

@@ -143,7 +143,7 @@ struct Call {
     uint8_t* quant_out;
     int32_t quant;       // arf::QuantMode
     const float* scale_in;
-    float* scale_out;
+    void* scale_out;
     bool reduce_only;
 };
 
@@ -168,7 +168,10 @@ arf_status validate(Call& c) {
     } else {
         if (!c.residual_in || !c.gamma) return ARF_ERR_NULL;
         if (c.quant == arf::kQuantTensor && (!c.quant_out || !c.scale_in)) return ARF_ERR_NULL;
-        if (c.quant == arf::kQuantToken && (!c.quant_out || !c.scale_out)) return ARF_ERR_NULL;
+        if ((c.quant == arf::kQuantToken || c.quant == arf::kQuantMx) &&
+            (!c.quant_out || !c.scale_out))
+            return ARF_ERR_NULL;
+        if (c.quant == arf::kQuantMx && c.hidden % 32 != 0) return ARF_ERR_SHAPE;
         if (c.quant == arf::kQuantNone && !c.residual_out && !c.norm_out)
             return ARF_ERR_NO_OUTPUT;
     }
@@ -189,8 +192,12 @@ arf_status validate(Call& c) {
     Range outs[4] = {
         c.residual_out ? span(c.residual_out, th * 2) : Range{0, 0},
         c.norm_out ? span(c.norm_out, th * 2) : Range{0, 0},
-        c.quant != arf::kQuantNone ? span(c.quant_out, th) : Range{0, 0},
-        c.quant == arf::kQuantToken ? span(c.scale_out, c.tokens * 4) : Range{0, 0},
+        c.quant == arf::kQuantMx      ? span(c.quant_out, th / 2)
+        : c.quant != arf::kQuantNone ? span(c.quant_out, th)
+                                     : Range{0, 0},
+        c.quant == arf::kQuantToken ? span(c.scale_out, c.tokens * 4)
+        : c.quant == arf::kQuantMx  ? span(c.scale_out, th / 32)
+                                    : Range{0, 0},
     };
     for (int i = 0; i < 4; ++i) {
         const Range o = outs[i];
@@ -318,13 +325,14 @@ arf_status arf_fused_epilogue(const arf_params* a, void* stream) {
     if (a->quant_out) {
         if (a->quant_mode == ARF_QUANT_PER_TENSOR) q = arf::kQuantTensor;
         else if (a->quant_mode == ARF_QUANT_PER_TOKEN) q = arf::kQuantToken;
+        else if (a->quant_mode == ARF_QUANT_MXFP4) q = arf::kQuantMx;
         else return ARF_ERR_VALUE;
     }
     Call c{a->partials, a->n_shards, a->tokens, a->row_begin, a->row_count, a->hidden,
            a->partial_dtype, a->act_dtype, a->accumulate, a->residual_in, a->residual_out,
            a->gamma, a->eps, a->norm_out, q != arf::kQuantNone ? a->quant_out : nullptr, q,
            q == arf::kQuantTensor ? a->scale_in : nullptr,
-           q == arf::kQuantToken ? a->scale_out : nullptr, false};
+           (q == arf::kQuantToken || q == arf::kQuantMx) ? a->scale_out : nullptr, false};
     return run(c, stream);
 }
 

@@ -210,3 +210,13 @@ def test_null_params_and_reduce_rows_validation():
     assert rr(P, 2, 4, 0, -1, 64, 0, 0, 0, RO + 4, None) == ALIGN
     assert rr(P, 2, 4, 4, -1, 64, 0, 0, 0, None, None) == OK      # empty range
     assert rr(P, 2, 0, 0, -1, 64, 0, 0, 0, None, None) == OK
+
+
+def test_mxfp4_validation():
+    # hidden not a multiple of 32, missing scale buffer, overlap of the block scales
+    assert callp(q=Q, mode=2, sout=S, hidden=40) == SHAPE
+    assert callp(q=Q, mode=2, sout=None) == NULL
+    assert callp(q=Q, mode=2, sout=Q + 64) == ALIAS
+    assert callp(q=Q, mode=2, sout=S + 1, tokens=0) == OK
+    # the fp8-only entry point does not take the MX mode
+    assert callq(mode=2) == VALUE

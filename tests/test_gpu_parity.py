@@ -450,3 +450,79 @@ def test_reduce_rows_and_twoshot_composition(pd, ad):
     for k in one:
         assert np.array_equal(two[k], one[k]), k
     compare(one, run_oracle(p, r, g, w.eps, pd, ad, quant="per_token"), "oneshot")
+
+
+# ---- OCP MXFP4 copy ------------------------------------------------------------------------
+
+def _ord4(c):
+    c = np.asarray(c, dtype=np.int32)
+    return np.where(c & 8, -(c & 7), c)
+
+
+def run_gpu_mx(p, r, g, eps, act):
+    from helpers import unpack_fp4
+    t, h = r.shape
+    rout, nout = Out((t, h), TORCH[act]), Out((t, h), TORCH[act])
+    q, sc = Out((t, h // 2), torch.uint8), Out((t, h // 32), torch.uint8)
+    arf.arf_fused_epilogue(p, r, g, eps, residual_out=rout.t, norm_out=nout.t, quant_out=q.t,
+                           mode=arf.ARF_QUANT_MXFP4, scale_out=sc.t)
+    torch.cuda.synchronize()
+    assert all(o.canary_ok() for o in (rout, nout, q, sc))
+    return {"residual_out": workloads.to_bits(rout.t), "norm_out": workloads.to_bits(nout.t),
+            "codes": unpack_fp4(q.t.cpu().numpy()), "scales": sc.t.cpu().numpy()}
+
+
+def compare_mx(got, ref, label=""):
+    from helpers import unpack_fp4
+    compare({k: got[k] for k in ("residual_out", "norm_out")},
+            {k: ref[k] for k in ("residual_out", "norm_out")}, label)
+    assert np.array_equal(got["scales"], ref["scale_out"]), label
+    d = np.abs(_ord4(got["codes"]) - _ord4(unpack_fp4(ref["quant_out"])))
+    assert d.max() <= 1, label
+    return float((d == 0).mean())
+
+
+@pytest.mark.parametrize("pd,ad", [("bf16", "bf16"), ("f16", "f16"), ("f32", "bf16"),
+                                   ("f32", "f16")])
+def test_mxfp4_parity(pd, ad):
+    for n, t, h in ((1, 3, 32), (2, 5, 1024), (8, 17, 4096), (4, 9, 7168), (3, 2, 16384)):
+        w = _case(n, t, h, pd, ad, 800 + h + n, std=2.0)
+        say("mxfp4 n=%d t=%d h=%d %s/%s" % (n, t, h, pd, ad))
+        (p, r, g), (pd_, rd, gd) = upload(w)
+        ref = run_oracle(p, r, g, w.eps, pd, ad, quant="mxfp4")
+        exact = compare_mx(run_gpu_mx(pd_, rd, gd, w.eps, ad), ref, "h=%d" % h)
+        assert exact >= 0.999
+
+
+@pytest.mark.parametrize("pd", ["bf16", "f32"])
+def test_mxfp4_every_geometry(pd):
+    h = 7168
+    w = _case(8, 6, h, pd, "bf16", 900, std=3.0)
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    ref = run_oracle(p, r, g, w.eps, pd, "bf16", quant="mxfp4")
+    try:
+        for path, wv, c in _geometries(h):
+            say("mxfp4 geometry %s path=%d waves=%d chunks=%d" % (pd, path, wv, c))
+            arf.arf_set_path_override(path, wv if path == 2 else 0, c)
+            compare_mx(run_gpu_mx(pd_, rd, gd, w.eps, "bf16"), ref, "geometry %s" % ((path, wv, c),))
+    finally:
+        arf.arf_set_path_override(0)
+
+
+def test_mxfp4_zero_rows_and_full_size_sample():
+    say("mxfp4 zero rows")
+    h = 2048
+    z = torch.zeros((2, 3, h), dtype=torch.bfloat16, device=DEV)
+    got = run_gpu_mx(z, z[0].clone(), torch.ones(h, dtype=torch.bfloat16, device=DEV), 1e-6, "bf16")
+    assert np.all(got["scales"] == 0) and np.all((got["codes"] & 7) == 0)
+    say("mxfp4 c4-size sampled rows")
+    w = workloads.WORKLOADS["c4"]
+    p, r, g = workloads.generate(w, DEV)
+    t = w.tokens
+    got = run_gpu_mx(p, r, g, w.eps, "bf16")
+    rows = sorted(set([0, t - 1] + list(np.random.default_rng(5).choice(t, 14, replace=False))))
+    idx = torch.tensor(rows, device=DEV)
+    ref = run_oracle(p[:, idx].contiguous(), r[idx].contiguous(), g, w.eps, "bf16", "bf16",
+                     quant="mxfp4")
+    compare_mx({k: v[rows] for k, v in got.items()}, ref, "c4 sample")
+    del p, r
