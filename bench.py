@@ -217,6 +217,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "io_dtype": w.partial_dtype if w.partial_dtype == w.act_dtype else
+                    "%s partials, %s activations" % (w.partial_dtype, w.act_dtype),
         "data": "synthetic",
         "config": {"workload": w.name, "n_shards": w.n_shards, "tokens": t, "hidden": h,
                    "partial_dtype": w.partial_dtype, "act_dtype": w.act_dtype,

@@ -526,3 +526,44 @@ def test_mxfp4_zero_rows_and_full_size_sample():
                      quant="mxfp4")
     compare_mx({k: v[rows] for k, v in got.items()}, ref, "c4 sample")
     del p, r
+
+
+# ---- size extremes ---------------------------------------------------------------------------
+
+def test_many_tokens_small_rows():
+    # 300000 rows of 64: a grid of hundreds of thousands of workgroups (or wavefront rows)
+    w = _case(2, 300000, 64, "bf16", "bf16", 1000, quant="per_token")
+    say("many tokens t=300000 h=64")
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    ref = run_oracle(p, r, g, w.eps, "bf16", "bf16", quant="per_token")
+    compare(run_gpu(pd_, rd, gd, w.eps, "bf16", quant="per_token"), ref, "t=300000")
+    try:   # the same through one row per wavefront
+        arf.arf_set_path_override(1)
+        compare(run_gpu(pd_, rd, gd, w.eps, "bf16", quant="per_token"), ref, "t=300000 per wave")
+    finally:
+        arf.arf_set_path_override(0)
+
+
+def test_partials_above_4_gib():
+    # 16 shards x 16384 x 16384 bf16 = 8 GiB of partials: 64-bit offsets beyond 2^32 bytes
+    w = workloads.Workload("huge", 16, 16384, 16384, "bf16", "bf16", 1.0, 1.0, 1e-6,
+                           "per_token", 77)
+    say("partials of 8 GiB (n=16 t=16384 h=16384)")
+    p, r, g = workloads.generate(w, DEV)
+    t, h = w.tokens, w.hidden
+    rout = torch.empty((t, h), dtype=torch.bfloat16, device=DEV)
+    nout = torch.empty((t, h), dtype=torch.bfloat16, device=DEV)
+    q = torch.empty((t, h), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((t,), dtype=torch.float32, device=DEV)
+    arf.arf_reduce_add_rmsnorm_quant(p, r, g, w.eps, q, arf.ARF_QUANT_PER_TOKEN, scale_out=sc,
+                                     residual_out=rout, norm_out=nout)
+    torch.cuda.synchronize()
+    rows = [0, 1, 8191, 8192, 12345, t - 1]
+    idx = torch.tensor(rows, device=DEV)
+    ref = run_oracle(p[:, idx].contiguous(), r[idx].contiguous(), g, w.eps, "bf16", "bf16",
+                     quant="per_token")
+    got = {"residual_out": workloads.to_bits(rout[idx]), "norm_out": workloads.to_bits(nout[idx]),
+           "quant_out": q[idx].cpu().numpy(), "scale_out": sc[idx].cpu().numpy()}
+    compare(got, ref, "8 GiB partials")
+    del p, r, rout, nout, q
+    torch.cuda.empty_cache()
