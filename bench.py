@@ -257,6 +257,45 @@ def _events_ms(fn, stream, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def graph_replay_us(launches=50, replays=20):
+    """Per-launch time of the decode-size workloads (c0, c1, c2) when `launches` calls are
+    captured in one HIP graph and the graph is replayed: the kernels' back-to-back time
+    without host launch overhead."""
+    import torch
+
+    import workloads
+
+    res = {}
+    dev = torch.device("cuda:0")
+    side = torch.cuda.Stream(device=dev)
+    for key in ("c0", "c1", "c2"):
+        w = workloads.WORKLOADS[key]
+        run = Runner(w, dev, side, sets=1)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run.step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        run.stream = None   # launch on the capturing (current) stream
+        with torch.cuda.graph(graph, stream=side):
+            for _ in range(launches):
+                run.step()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (replays * launches)
+        res[w.name] = {"us_per_launch": round(us, 3),
+                       "achieved_GBs": round(w.algorithmic_bytes() / (us * 1e-6) / 1e9, 1)}
+        del graph, run
+    return res
+
+
 def measure_variants(w, run, stream, steps, warmup):
     """The same workload with accumulation in the partial type, and one rank's share of
     the token-slice exchange (reduce T/N rows of the N shards; then the epilogue over
@@ -305,6 +344,9 @@ def measure_variants(w, run, stream, steps, warmup):
         "epilogue_ms": round(ms_e, 5), "epilogue_achieved": round(b_e / (ms_e * 1e-3) / 1e9, 2),
         "unit": "GB/s"}
     del sums
+
+    # decode-size calls replayed from a HIP graph (no per-launch host overhead)
+    out["graph_replay"] = graph_replay_us()
 
     # the block-scaled 4-bit copy in place of the fp8 one
     if h % 32 == 0:

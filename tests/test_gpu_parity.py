@@ -567,3 +567,41 @@ def test_partials_above_4_gib():
     compare(got, ref, "8 GiB partials")
     del p, r, rout, nout, q
     torch.cuda.empty_cache()
+
+
+# ---- HIP graph capture --------------------------------------------------------------------
+
+def test_graph_capture_and_replay():
+    # the fused call captured into a graph on a side stream, replayed with eager work
+    # (poisoning the outputs) in between; every replay must equal the eager result
+    w = workloads.WORKLOADS["c1"]
+    say("graph capture / replay %s" % w.name)
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    t, h = w.tokens, w.hidden
+    eager = run_gpu(pd_, rd, gd, w.eps, "bf16", quant="per_token")
+    rout = torch.empty((t, h), dtype=torch.bfloat16, device=DEV)
+    nout = torch.empty((t, h), dtype=torch.bfloat16, device=DEV)
+    q = torch.empty((t, h), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((t,), dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up launch outside the capture
+        arf.arf_reduce_add_rmsnorm_quant(pd_, rd, gd, w.eps, q, arf.ARF_QUANT_PER_TOKEN,
+                                         scale_out=sc, residual_out=rout, norm_out=nout)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        arf.arf_reduce_add_rmsnorm_quant(pd_, rd, gd, w.eps, q, arf.ARF_QUANT_PER_TOKEN,
+                                         scale_out=sc, residual_out=rout, norm_out=nout)
+    for k in range(4):
+        for o in (rout, nout):
+            o.view(torch.int16).fill_(-1)
+        q.fill_(0xFF)
+        sc.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {"residual_out": workloads.to_bits(rout), "norm_out": workloads.to_bits(nout),
+               "quant_out": q.cpu().numpy(), "scale_out": sc.cpu().numpy()}
+        for key in eager:
+            assert np.array_equal(got[key], eager[key]), (k, key)
