@@ -122,7 +122,8 @@ def parse():
     ap.add_argument("--workload", default="c4", help="c0..c4 (default c4)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target oracle time for the CPU baseline (0: skip it)")
-    ap.add_argument("--no-copy-probe", action="store_true")
+    ap.add_argument("--no-copy-probe", action="store_true",
+                    help="skip the HBM probes (read, write, copy, workload mix)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the accumulation and token-slice variants")
     ap.add_argument("--secondary", default="c3",
@@ -157,24 +158,6 @@ def main():
     traffic = read_traffic(w.name)
     p, r, g, rout, nout, q, sc_out, sc_in = run.sets[0]
 
-    # HBM ceiling probe: a streaming copy of 1 GiB with the same load/store forms
-    copy = None
-    if not args.no_copy_probe:
-        nb = 1 << 30
-        src = torch.empty(nb, dtype=torch.uint8, device=dev).random_(0, 256)
-        dst = torch.empty(nb, dtype=torch.uint8, device=dev)
-        for _ in range(3):
-            arf.arf_stream_copy(dst, src, nb, stream=stream)
-        c0 = torch.cuda.Event(enable_timing=True)
-        c1 = torch.cuda.Event(enable_timing=True)
-        c0.record(stream)
-        for _ in range(10):
-            arf.arf_stream_copy(dst, src, nb, stream=stream)
-        c1.record(stream)
-        torch.cuda.synchronize()
-        copy = 2 * nb / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
-        del src, dst
-
     secondary = None
     if args.secondary:
         w2 = workloads.WORKLOADS[args.secondary]
@@ -204,6 +187,10 @@ def main():
     if not args.no_variants:
         variants = measure_variants(w, run, stream, max(args.steps, 10), args.warmup)
 
+    probes = None
+    if not args.no_copy_probe:
+        probes = hbm_probes(w, p, stream)
+
     plan = arf.arf_get_plan(w.n_shards, t, h, {"bf16": 0, "f16": 1, "f32": 2}[w.partial_dtype])
     line = {
         "metric": METRIC,
@@ -230,8 +217,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
-        "hbm_copy_ceiling_GBs": None if copy is None else round(copy, 1),
-        "frac_of_copy_ceiling": None if copy is None else round(achieved / copy, 4),
+        "hbm_probes": probes,
+        "frac_of_mix_ceiling": None if probes is None else round(achieved / probes["mix_GBs"], 4),
         "secondary": secondary,
         "variants": variants,
         "cpu_baseline": cpu,
@@ -239,6 +226,54 @@ def main():
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def hbm_probes(w, partials, stream, reps=10):
+    """HBM ceilings from streaming kernels with no arithmetic (GB/s): read only, write
+    only, a copy, and the workload's own mix -- reading the partials buffer and writing
+    a buffer in the workload's write:read ratio, in one unit per row (reads, then writes,
+    per unit), as the fused kernel does."""
+    import torch
+
+    import shard_reduce_residual_amd as arf
+
+    dev = partials.device
+    read_b = partials.numel() * partials.element_size()
+    B = w.algorithmic_bytes()
+    n, t, h = w.n_shards, w.tokens, w.hidden
+    alg_read = n * t * h * w.sp + t * h * w.sa + h * w.sa + (4 if w.quant == "per_tensor" else 0)
+    alg_write = B - alg_read
+    mix_write = (int(read_b * alg_write / alg_read) // 16) * 16
+    one_gib = 1 << 30
+    dst = torch.empty(max(mix_write, one_gib), dtype=torch.uint8, device=dev)
+    src2 = partials.view(torch.uint8).view(-1)[:one_gib]
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    out = {}
+    t_r = timed(lambda: arf.arf_stream_mix(None, 0, partials, read_b, stream=stream))
+    out["read_GBs"] = round(read_b / t_r / 1e9, 1)
+    t_w = timed(lambda: arf.arf_stream_mix(dst, one_gib, None, 0, stream=stream))
+    out["write_GBs"] = round(one_gib / t_w / 1e9, 1)
+    t_c = timed(lambda: arf.arf_stream_copy(dst, src2, one_gib, stream=stream))
+    out["copy_GBs"] = round(2 * one_gib / t_c / 1e9, 1)
+    t_m = timed(lambda: arf.arf_stream_mix(dst, mix_write, partials, read_b, units=t,
+                                           stream=stream))
+    out["mix_GBs"] = round((read_b + mix_write) / t_m / 1e9, 1)
+    out["mix_read_fraction"] = round(read_b / (read_b + mix_write), 4)
+    out["mix_units"] = t
+    del dst
+    return out
 
 
 def _events_ms(fn, stream, steps, warmup):

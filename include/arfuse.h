@@ -223,6 +223,18 @@ arf_status arf_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* strea
  */
 arf_status arf_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
 
+/*
+ * Streaming probe with a chosen read/write mix, for the HBM ceiling of a traffic pattern:
+ * reads read_bytes from src and writes write_bytes to dst, with no arithmetic, in `units`
+ * work units (one workgroup each). Unit u reads its share of src in order, then writes
+ * its share of dst with values derived from what it read, the way a row of the fused
+ * kernel reads its inputs before writing its outputs. Byte counts are multiples of 16
+ * (either may be 0); pointers 16-byte aligned; the ranges must not overlap; units <= 0
+ * picks one unit per 16 KiB of the smaller non-zero side. dst receives unspecified bytes.
+ */
+arf_status arf_stream_mix(void* dst, int64_t write_bytes, const void* src, int64_t read_bytes,
+                          int64_t units, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

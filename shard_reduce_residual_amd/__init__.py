@@ -48,6 +48,7 @@ SIGNATURES = {
     "arf_set_path_override": (_i32, [_i32, _i32, _i32]),
     "arf_e4m3_encode": (_i32, [_vp, _vp, _i64, _vp]),
     "arf_stream_copy": (_i32, [_vp, _vp, _i64, _vp]),
+    "arf_stream_mix": (_i32, [_vp, _i64, _vp, _i64, _i64, _vp]),
 }
 
 
@@ -185,3 +186,10 @@ def arf_stream_copy(dst, src, nbytes: int | None = None, stream=None) -> None:
     nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
     _check(lib().arf_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)),
            "arf_stream_copy")
+
+
+def arf_stream_mix(dst, write_bytes: int, src, read_bytes: int, units: int = 0,
+                   stream=None) -> None:
+    _check(lib().arf_stream_mix(_ptr(dst) if write_bytes else None, write_bytes,
+                                _ptr(src) if read_bytes else None, read_bytes, units,
+                                _stream(stream)), "arf_stream_mix")

@@ -284,6 +284,47 @@ __global__ __launch_bounds__(256) void stream_copy_kernel(char* __restrict__ dst
     }
 }
 
+// Streaming probe with a given read/write mix: unit u reads its share of src (16 KiB
+// spans, non-temporal), then writes its share of dst with a value that depends on what it
+// read, so each unit's writes follow its reads as in the fused kernel's rows.
+constexpr int kMixUnroll = 4;
+constexpr int64_t kMixSpan = 256 * kMixUnroll * 16;
+
+__global__ __launch_bounds__(256) void stream_mix_kernel(char* __restrict__ dst,
+                                                         int64_t write_bytes,
+                                                         const char* __restrict__ src,
+                                                         int64_t read_bytes, int64_t units) {
+    const int64_t sr = (read_bytes + kMixSpan - 1) / kMixSpan;
+    const int64_t sw = (write_bytes + kMixSpan - 1) / kMixSpan;
+    for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+        uint32_t acc = (uint32_t)u;
+        for (int64_t k = u * sr / units; k < (u + 1) * sr / units; ++k) {
+            const int64_t left = read_bytes - k * kMixSpan;
+            const auto rs = arf::make_rsrc(src + k * kMixSpan,
+                                           (uint32_t)(left < kMixSpan ? left : kMixSpan));
+            arf::u32x4 v[kMixUnroll];
+#pragma unroll
+            for (int i = 0; i < kMixUnroll; ++i)
+                v[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rs, (uint32_t)(i * 256 + threadIdx.x) * 16u, 0, arf::kAuxStream);
+#pragma unroll
+            for (int i = 0; i < kMixUnroll; ++i) acc ^= v[i][0] ^ v[i][1] ^ v[i][2] ^ v[i][3];
+        }
+        // keep the loads live when nothing is written (an empty statement, no instruction)
+        __asm__ volatile("" : : "v"(acc));
+        const arf::u32x4 w = {acc, acc + 1u, acc + 2u, acc + 3u};
+        for (int64_t k = u * sw / units; k < (u + 1) * sw / units; ++k) {
+            const int64_t left = write_bytes - k * kMixSpan;
+            const auto rd = arf::make_rsrc(dst + k * kMixSpan,
+                                           (uint32_t)(left < kMixSpan ? left : kMixSpan));
+#pragma unroll
+            for (int i = 0; i < kMixUnroll; ++i)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    w, rd, (uint32_t)(i * 256 + threadIdx.x) * 16u, 0, arf::kAuxStream);
+        }
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -430,6 +471,33 @@ arf_status arf_stream_copy(void* dst, const void* src, int64_t bytes, void* stre
     const char* s = (const char*)src;
     void* args[] = {&d, &s, &bytes};
     return hipLaunchKernel(reinterpret_cast<const void*>(&stream_copy_kernel), dim3(grid),
+                           dim3(256), args, 0, (hipStream_t)stream) == hipSuccess
+               ? ARF_OK
+               : ARF_ERR_HIP;
+}
+
+arf_status arf_stream_mix(void* dst, int64_t write_bytes, const void* src, int64_t read_bytes,
+                          int64_t units, void* stream) {
+    if (read_bytes < 0 || write_bytes < 0 || read_bytes % 16 != 0 || write_bytes % 16 != 0)
+        return ARF_ERR_SHAPE;
+    if (read_bytes == 0 && write_bytes == 0) return ARF_OK;
+    if ((read_bytes && !src) || (write_bytes && !dst)) return ARF_ERR_NULL;
+    if ((read_bytes && !aligned(src, 16)) || (write_bytes && !aligned(dst, 16)))
+        return ARF_ERR_ALIGN;
+    if (read_bytes && write_bytes && overlap(span(dst, write_bytes), span(src, read_bytes)))
+        return ARF_ERR_ALIAS;
+    const int64_t sr = (read_bytes + kMixSpan - 1) / kMixSpan;
+    const int64_t sw = (write_bytes + kMixSpan - 1) / kMixSpan;
+    if (units <= 0) units = sr && sw ? (sr < sw ? sr : sw) : (sr ? sr : sw);
+    if (units > INT32_MAX) return ARF_ERR_SHAPE;
+    int cus = 0;
+    arf_status st = device_cus(&cus);
+    if (st != ARF_OK) return st;
+    const uint32_t grid = (uint32_t)units;
+    char* d = (char*)dst;
+    const char* sp = (const char*)src;
+    void* args[] = {&d, &write_bytes, &sp, &read_bytes, &units};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&stream_mix_kernel), dim3(grid),
                            dim3(256), args, 0, (hipStream_t)stream) == hipSuccess
                ? ARF_OK
                : ARF_ERR_HIP;

@@ -27,7 +27,7 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     L = arf.lib()
     names = declared_symbols()
-    assert len(names) == 10
+    assert len(names) == 11
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(arf.SIGNATURES)
@@ -220,3 +220,15 @@ def test_mxfp4_validation():
     assert callp(q=Q, mode=2, sout=S + 1, tokens=0) == OK
     # the fp8-only entry point does not take the MX mode
     assert callq(mode=2) == VALUE
+
+
+def test_stream_mix_validation():
+    L = arf.lib()
+    assert L.arf_stream_mix(None, 0, None, 0, 0, None) == OK
+    assert L.arf_stream_mix(Q, 24, P, 32, 0, None) == SHAPE
+    assert L.arf_stream_mix(Q, -16, P, 32, 0, None) == SHAPE
+    assert L.arf_stream_mix(None, 32, P, 32, 0, None) == NULL
+    assert L.arf_stream_mix(Q, 32, None, 32, 0, None) == NULL
+    assert L.arf_stream_mix(Q + 8, 32, P, 32, 0, None) == ALIGN
+    assert L.arf_stream_mix(P + 16, 64, P, 64, 0, None) == ALIAS
+    assert L.arf_stream_mix(Q, 16, P, 16, 2 ** 40, None) == SHAPE

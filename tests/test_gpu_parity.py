@@ -605,3 +605,17 @@ def test_graph_capture_and_replay():
                "quant_out": q.cpu().numpy(), "scale_out": sc.cpu().numpy()}
         for key in eager:
             assert np.array_equal(got[key], eager[key]), (k, key)
+
+
+def test_stream_mix_writes_exactly_its_range():
+    for rb, wb, units in ((1 << 20, 1 << 18, 0), (3 * 16384 + 48, 0, 0), (0, 5 * 16384 + 16, 3),
+                          (64 << 20, 16 << 20, 1024)):
+        say("stream mix read %d write %d units %d" % (rb, wb, units))
+        src = torch.randint(0, 256, (max(rb, 16),), dtype=torch.uint8, device=DEV)
+        dst = torch.full((wb + GUARD,), CANARY, dtype=torch.uint8, device=DEV)
+        arf.arf_stream_mix(dst, wb, src, rb, units)
+        torch.cuda.synchronize()
+        assert bool((dst[wb:] == CANARY).all())
+        if wb:   # every 16-byte word of the range was written (none keeps the canary)
+            words = dst[:wb].view(-1, 16)
+            assert not bool((words == CANARY).all(dim=1).any())
