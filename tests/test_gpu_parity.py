@@ -619,3 +619,35 @@ def test_stream_mix_writes_exactly_its_range():
         if wb:   # every 16-byte word of the range was written (none keeps the canary)
             words = dst[:wb].view(-1, 16)
             assert not bool((words == CANARY).all(dim=1).any())
+
+
+# ---- special values ---------------------------------------------------------------------------
+
+def _same_or_both_nan16(a, b, act):
+    fa, fb = oracle.act_to_f32(a, act), oracle.act_to_f32(b, act)
+    both_nan = np.isnan(fa) & np.isnan(fb)
+    return bool(np.all(both_nan | (a == b)))
+
+
+@pytest.mark.parametrize("value", ["nan", "inf", "-inf", "negzero"])
+def test_special_values_match_the_oracle(value):
+    say("special value %s" % value)
+    w = _case(4, 6, 1024, "bf16", "bf16", 1100, quant="per_token")
+    p, r, g = workloads.generate(w, "cpu")
+    p = p.clone()
+    if value == "negzero":
+        p.fill_(-0.0)
+        r = torch.full_like(r, -0.0)
+    else:
+        p[2, 3, 17] = float(value)
+        p[0, 5, 1000] = float(value)
+    ref = run_oracle(p, r, g, w.eps, "bf16", "bf16", quant="per_token")
+    got = run_gpu(p.to(DEV), r.to(DEV), g.to(DEV), w.eps, "bf16", quant="per_token")
+    assert _same_or_both_nan16(got["residual_out"], ref["residual_out"], "bf16")
+    assert _same_or_both_nan16(got["norm_out"], ref["norm_out"], "bf16")
+    qg, qr = got["quant_out"], ref["quant_out"]
+    nan_codes = (qr & 0x7F) == 0x7F
+    assert np.array_equal((qg & 0x7F) == 0x7F, nan_codes)
+    assert np.array_equal(qg[~nan_codes], qr[~nan_codes])
+    sg, sr = got["scale_out"], ref["scale_out"]
+    assert np.array_equal(np.isnan(sg), np.isnan(sr)) and np.array_equal(sg[~np.isnan(sr)], sr[~np.isnan(sr)])

@@ -313,3 +313,53 @@ def test_generator_is_reproducible_and_has_the_stated_moments():
     assert abs(p.std().item() - 0.5) < 0.01 and abs(a[1].float().std().item() - 1.0) < 0.02
     gmin, gmax = a[2].float().min().item(), a[2].float().max().item()
     assert 0.5 <= gmin and gmax <= 1.5
+
+
+# ---- special values (IEEE 754 propagation through the method's steps) -----------------------
+
+def _special_case(value, act="bf16"):
+    w = workloads.WORKLOADS["c0"].with_tokens(3)
+    p, r, g = (workloads.to_bits(x) for x in workloads.generate(w, "cpu"))
+    p = p.copy()
+    p[1, 1, 5] = _act_bits([value], act)[0] if np.isfinite(value) else \
+        (0x7FC0 if np.isnan(value) else (0x7F80 if value > 0 else 0xFF80))
+    return w, p, r, g
+
+
+def test_nan_partial_poisons_its_element_and_its_row_norm():
+    w, p, r, g = _special_case(float("nan"))
+    out = _run(p, r, g, w.eps, "bf16", "bf16", quant="per_token")
+    x = act_bits_to_f64(out["residual_out"], "bf16")
+    y = act_bits_to_f64(out["norm_out"], "bf16")
+    assert np.isnan(x[1, 5]) and np.isnan(x).sum() == 1
+    assert np.all(np.isnan(y[1])) and not np.any(np.isnan(y[[0, 2]]))
+    # the per-token max skips NaN; every code of the row is a NaN code
+    assert np.all((out["quant_out"][1] & 0x7F) == 0x7F)
+    assert not np.isnan(out["scale_out"][1])
+
+
+def test_infinite_partial_gives_zero_inverse_root():
+    w, p, r, g = _special_case(float("inf"))
+    out = _run(p, r, g, w.eps, "bf16", "bf16")
+    x = act_bits_to_f64(out["residual_out"], "bf16")
+    y = act_bits_to_f64(out["norm_out"], "bf16")
+    assert x[1, 5] == np.inf
+    # sum of squares is inf, so 1/sqrt(.) = 0: finite elements give +-0, the inf one NaN
+    assert np.isnan(y[1, 5])
+    finite = np.delete(y[1], 5)
+    assert np.all(finite == 0.0)
+    assert np.array_equal(np.signbit(finite), np.signbit(np.delete(x[1], 5)))
+
+
+def test_negative_zeros_stay_negative():
+    h = 64
+    p = np.full((3, 2, h), 0x8000, np.uint16)
+    r = np.full((2, h), 0x8000, np.uint16)
+    g = _act_bits(np.ones(h), "bf16")
+    out = _run(p, r, g, 1e-6, "bf16", "bf16", quant="per_token")
+    assert np.all(out["residual_out"] == 0x8000)     # -0 + -0 = -0 at every step
+    assert np.all(out["norm_out"] == 0x8000)         # (-0 * inv) * 1 = -0
+    assert np.all(out["quant_out"] == 0x80) and np.all(out["scale_out"] == 0)
+    # +0 residual: -0 + +0 = +0
+    out = _run(p, np.zeros((2, h), np.uint16), g, 1e-6, "bf16", "bf16")
+    assert np.all(out["residual_out"] == 0x0000)
