@@ -113,6 +113,31 @@ class Runner:
         t1 = time.perf_counter()
         return (t1 - t0) * 1e3 / steps, ev0.elapsed_time(ev1) / steps
 
+    def distribution(self, launches, flush=None):
+        """Per-launch durations (ms, sorted) from an event pair around each launch on the
+        launch stream. ``flush()``, if given, runs before each pair, outside it."""
+        import torch
+
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(launches)]
+        for e0, e1 in ev:
+            if flush is not None:
+                flush()
+            e0.record(self.stream)
+            self.step()
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        return sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+
+
+def percentiles_us(ms_sorted):
+    """median, p10 and p90 (µs) of sorted per-launch durations in ms."""
+    def at(q):
+        return ms_sorted[min(len(ms_sorted) - 1, int(round(q * (len(ms_sorted) - 1))))] * 1e3
+    return {"median": round(at(0.5), 3), "p10": round(at(0.1), 3), "p90": round(at(0.9), 3),
+            "launches": len(ms_sorted)}
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
@@ -156,6 +181,7 @@ def main():
     value = B / (ms_per_step * 1e-3) / 1e9
     achieved = B / (kernel_ms * 1e-3) / 1e9
     traffic = read_traffic(w.name)
+    launch_us = percentiles_us(run.distribution(max(args.steps, 20)))
     p, r, g, rout, nout, q, sc_out, sc_in = run.sets[0]
 
     secondary = None
@@ -165,12 +191,14 @@ def main():
         # rotate enough buffer sets that the 256 MB Infinity Cache cannot serve a launch
         sets = max(1, min(8, -(-1_500_000_000 // B2)))
         run2 = Runner(w2, dev, stream, sets=sets)
-        steps2 = max(args.steps, 100)
+        steps2 = max(args.steps, 200)
         ms2, kms2 = run2.measure(steps2, max(args.warmup, 10))
+        launch2 = percentiles_us(run2.distribution(steps2))
         del run2
         torch.cuda.empty_cache()
         secondary = {"workload": w2.name, "buffer_sets": sets, "steps": steps2,
                      "ms_per_step": round(ms2, 5), "kernel_ms": round(kms2, 5),
+                     "launch_us": launch2,
                      "achieved": round(B2 / (kms2 * 1e-3) / 1e9, 2), "unit": "GB/s",
                      "frac": round(B2 / (kms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "tokens_per_s": round(w2.tokens / (kms2 * 1e-3), 1),
@@ -186,6 +214,10 @@ def main():
     variants = None
     if not args.no_variants:
         variants = measure_variants(w, run, stream, max(args.steps, 10), args.warmup)
+
+    decode = None
+    if not args.no_variants:
+        decode = decode_cold(stream)
 
     probes = None
     if not args.no_copy_probe:
@@ -213,6 +245,7 @@ def main():
         "tokens_per_s": round(t / (ms_per_step * 1e-3), 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "kernel_ms": round(kernel_ms, 5),
+        "launch_us": launch_us,
         "plan": plan,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -221,6 +254,7 @@ def main():
         "frac_of_mix_ceiling": None if probes is None else round(achieved / probes["mix_GBs"], 4),
         "secondary": secondary,
         "variants": variants,
+        "decode_cold": decode,
         "cpu_baseline": cpu,
         "sample_parity": parity,
     }
@@ -331,6 +365,47 @@ def graph_replay_us(launches=50, replays=20):
     return res
 
 
+def decode_cold(stream, launches=1000):
+    """Per-launch time of the decode-size workloads (c0, c1, c2) with their inputs out of
+    every cache: before each launch, outside its event pair, 1 GiB is written (four times
+    the 256 MB Infinity Cache), then one 16-byte write lets that flush's end-of-kernel
+    cache write-back finish before the first event. ``floor`` is a 16-byte write timed in
+    the same position: the part of each figure that any launch there costs."""
+    import torch
+
+    import shard_reduce_residual_amd as arf
+    import workloads
+
+    dev = torch.device("cuda:0")
+    one_gib = 1 << 30
+    junk = torch.empty(one_gib, dtype=torch.uint8, device=dev)
+
+    def flush():
+        arf.arf_stream_mix(junk, one_gib, None, 0, stream=stream)
+        arf.arf_stream_mix(junk, 16, None, 0, stream=stream)
+
+    class Tiny:   # a one-workgroup, 16-byte write: what any launch costs in this position
+        def __init__(self):
+            self.stream = stream
+
+        def step(self):
+            arf.arf_stream_mix(junk, 16, None, 0, stream=stream)
+
+    res = {"floor": percentiles_us(Runner.distribution(Tiny(), launches, flush=flush))}
+    for key in ("c0", "c1", "c2"):
+        w = workloads.WORKLOADS[key]
+        run = Runner(w, dev, stream, sets=1)
+        for _ in range(5):
+            run.step()
+        us = percentiles_us(run.distribution(launches, flush=flush))
+        us["achieved_GBs_at_median"] = round(w.algorithmic_bytes() / (us["median"] * 1e-6) / 1e9, 1)
+        res[w.name] = us
+        del run
+    del junk
+    torch.cuda.empty_cache()
+    return res
+
+
 def measure_variants(w, run, stream, steps, warmup):
     """The same workload with accumulation in the partial type, and one rank's share of
     the token-slice exchange (reduce T/N rows of the N shards; then the epilogue over
@@ -403,6 +478,16 @@ def measure_variants(w, run, stream, steps, warmup):
     return out
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(args, w, p, r, g, rout, nout, q, sc_out, sc_in):
     """Oracle on the first rows of the same workload, on the host's cores, repeated until
     about --cpu-seconds of work; also checks the GPU's outputs for those rows."""
@@ -428,11 +513,27 @@ def cpu_baseline(args, w, p, r, g, rout, nout, q, sc_out, sc_in):
         elapsed += time.perf_counter() - s
         passes += 1
     sample_bytes = w.with_tokens(rows).algorithmic_bytes()
+    # the same oracle on one thread, over the first eighth of those rows
+    rows1 = max(1, rows // 8)
+    kw1 = dict(kw, n_threads=1)
+    p1, r1 = ph[:, :rows1].copy(), rh[:rows1].copy()
+    passes1, elapsed1 = 0, 0.0
+    while elapsed1 < args.cpu_seconds / 4 and passes1 < 200:
+        s = time.perf_counter()
+        oracle.reduce_add_rmsnorm(p1, r1, gh, w.eps, **kw1)
+        elapsed1 += time.perf_counter() - s
+        passes1 += 1
     cpu = {"value": round(sample_bytes * passes / elapsed / 1e9, 3), "unit": "GB/s",
            "tokens_per_s": round(rows * passes / elapsed, 1), "cores": threads,
            "kind": "oracle",
            "sample": "first %d of %d tokens of %s, %d passes, %.1f s"
-                     % (rows, w.tokens, w.name, passes, elapsed)}
+                     % (rows, w.tokens, w.name, passes, elapsed),
+           "one_thread": {"value": round(w.with_tokens(rows1).algorithmic_bytes() * passes1
+                                         / elapsed1 / 1e9, 3),
+                          "tokens_per_s": round(rows1 * passes1 / elapsed1, 1),
+                          "sample": "first %d tokens, %d passes, %.1f s"
+                                    % (rows1, passes1, elapsed1)},
+           "cpu_model": cpu_model(), "host_cpus": oracle.default_threads()}
 
     def ordinal(b, bits):
         b = b.astype(np.int64)

@@ -6,19 +6,30 @@
 // Menu: shard count N in 1..16 (exact: no per-shard branch, so the loads of a whole row
 // are scheduled freely); one row per wavefront (4 wavefronts per workgroup) with C in
 // {1, 2, 4, 8}; one row per workgroup with WAVES in {4, 8, 16} and C in {1, 2, 4, 8}.
+// Every geometry has one kernel per (N, C); only its prefetch depth differs by geometry.
 #pragma once
 
 #include "arfuse_device.hpp"
 
 namespace arf {
 
+// Shards in flight per row. The 8-wave row-per-workgroup geometry is the plan's choice
+// when a launch has fewer than two rows per CU; there the time is load latency rather than
+// HBM throughput, so its kernels keep up to three shards in flight (bounded by the load
+// registers, C * pieces * 4 VGPRs per slot) instead of one.
+template <class PT, int C, int W>
+constexpr int block_depth() {
+    constexpr int pc = C * PartTraits<PT>::kPieces;
+    return W != 8 ? 2 : (pc <= 4 ? 4 : (pc <= 8 ? 3 : 2));
+}
+
 template <class PT, class AT, int N, int W>
 launch_fn pick_block_c(int c) {
     switch (c) {
-        case 1: return &launch_fused<PT, AT, N, 1, W, false>;
-        case 2: return &launch_fused<PT, AT, N, 2, W, false>;
-        case 4: return &launch_fused<PT, AT, N, 4, W, false>;
-        case 8: return &launch_fused<PT, AT, N, 8, W, false>;
+        case 1: return &launch_fused<PT, AT, N, 1, W, false, block_depth<PT, 1, W>()>;
+        case 2: return &launch_fused<PT, AT, N, 2, W, false, block_depth<PT, 2, W>()>;
+        case 4: return &launch_fused<PT, AT, N, 4, W, false, block_depth<PT, 4, W>()>;
+        case 8: return &launch_fused<PT, AT, N, 8, W, false, block_depth<PT, 8, W>()>;
         default: return nullptr;
     }
 }
