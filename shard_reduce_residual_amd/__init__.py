@@ -94,6 +94,35 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _dev(name, t, device, numel=None, dtypes=None):
+    """Device pointer of ``t`` after the checks the C ABI cannot make: a contiguous tensor
+    on ``device`` (a host pointer handed to a kernel would fault the GPU), with ``numel``
+    elements of one of ``dtypes`` (a short buffer would be written past its end). None
+    stays None (an optional buffer left out)."""
+    if t is None:
+        return None
+    if t.device != device:
+        raise ValueError("%s is on %s; the call runs on %s" % (name, t.device, device))
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s; expected %s" % (name, t.dtype, dtypes))
+    if numel is not None and t.numel() != numel:
+        raise ValueError("%s has %d elements; expected %d" % (name, t.numel(), numel))
+    return _ptr(t)
+
+
+def _partials(partials):
+    if partials.dim() != 3:
+        raise ValueError("partials must be [n_shards][tokens][hidden]")
+    if partials.device.type != "cuda":
+        raise ValueError("partials must be a device tensor (got %s)" % partials.device)
+    return partials.shape
+
+
+def _act_dtypes():
+    import torch
+    return (torch.bfloat16, torch.float16)
+
+
 def _stream(stream):
     import torch
     if stream is None:
@@ -112,11 +141,15 @@ def arf_reduce_add_rmsnorm(partials, residual_in, gamma, eps: float, residual_ou
                            norm_out=None, stream=None) -> None:
     """partials [N][T][H] (bf16/f16, or f32); residual_in/_out, norm_out [T][H] and
     gamma [H] in the activation type. Enqueues one kernel on ``stream``."""
-    n, t, h = partials.shape
+    n, t, h = _partials(partials)
+    dev, act = partials.device, (residual_in.dtype,)
     st = lib().arf_reduce_add_rmsnorm(_ptr(partials), n, t, h, _dtype_code(partials),
-                                      _dtype_code(residual_in), _ptr(residual_in),
-                                      _ptr(residual_out), _ptr(gamma), float(eps),
-                                      _ptr(norm_out), _stream(stream))
+                                      _dtype_code(residual_in),
+                                      _dev("residual_in", residual_in, dev, t * h, _act_dtypes()),
+                                      _dev("residual_out", residual_out, dev, t * h, act),
+                                      _dev("gamma", gamma, dev, h, act), float(eps),
+                                      _dev("norm_out", norm_out, dev, t * h, act),
+                                      _stream(stream))
     _check(st, "arf_reduce_add_rmsnorm")
 
 
@@ -126,11 +159,18 @@ def arf_reduce_add_rmsnorm_quant(partials, residual_in, gamma, eps: float, quant
     """As arf_reduce_add_rmsnorm plus ``quant_out`` [T][H] uint8 E4M3 codes;
     ``mode`` ARF_QUANT_PER_TENSOR (``scale_in``: 1-element f32 device tensor) or
     ARF_QUANT_PER_TOKEN (``scale_out``: [T] f32 device tensor, written)."""
-    n, t, h = partials.shape
+    import torch
+    n, t, h = _partials(partials)
+    dev, act = partials.device, (residual_in.dtype,)
     st = lib().arf_reduce_add_rmsnorm_quant(
         _ptr(partials), n, t, h, _dtype_code(partials), _dtype_code(residual_in),
-        _ptr(residual_in), _ptr(residual_out), _ptr(gamma), float(eps), _ptr(norm_out),
-        _ptr(quant_out), int(mode), _ptr(scale_in), _ptr(scale_out), _stream(stream))
+        _dev("residual_in", residual_in, dev, t * h, _act_dtypes()),
+        _dev("residual_out", residual_out, dev, t * h, act),
+        _dev("gamma", gamma, dev, h, act), float(eps),
+        _dev("norm_out", norm_out, dev, t * h, act),
+        _dev("quant_out", quant_out, dev, t * h, (torch.uint8,)), int(mode),
+        _dev("scale_in", scale_in, dev, 1, (torch.float32,)),
+        _dev("scale_out", scale_out, dev, t, (torch.float32,)), _stream(stream))
     _check(st, "arf_reduce_add_rmsnorm_quant")
 
 
@@ -139,21 +179,32 @@ def arf_fused_epilogue(partials, residual_in, gamma, eps: float, residual_out=No
                        scale_in=None, scale_out=None, accumulate: int = ARF_ACC_F32,
                        row_begin: int = 0, row_count: int = -1, stream=None) -> None:
     """The general call: row range and accumulation mode (see arf_params)."""
-    n, t, h = partials.shape
+    import torch
+    n, t, h = _partials(partials)
+    dev, act = partials.device, (residual_in.dtype,)
+    mx = quant_out is not None and mode == ARF_QUANT_MXFP4
     a = arf_params(ctypes.sizeof(arf_params), n, _ptr(partials), t, row_begin, row_count, h,
                    _dtype_code(partials), _dtype_code(residual_in), accumulate,
-                   _ptr(residual_in), _ptr(residual_out), _ptr(gamma), float(eps),
-                   _ptr(norm_out), _ptr(quant_out), mode, _ptr(scale_in), _ptr(scale_out))
+                   _dev("residual_in", residual_in, dev, t * h, _act_dtypes()),
+                   _dev("residual_out", residual_out, dev, t * h, act),
+                   _dev("gamma", gamma, dev, h, act), float(eps),
+                   _dev("norm_out", norm_out, dev, t * h, act),
+                   _dev("quant_out", quant_out, dev, t * h // 2 if mx else t * h,
+                        (torch.uint8,)), mode,
+                   _dev("scale_in", scale_in, dev, 1, (torch.float32,)),
+                   _dev("scale_out", scale_out, dev, t * h // 32 if mx else t,
+                        (torch.uint8,) if mx else (torch.float32,)))
     _check(lib().arf_fused_epilogue(ctypes.byref(a), _stream(stream)), "arf_fused_epilogue")
 
 
 def arf_reduce_rows(partials, sums_out, row_begin: int = 0, row_count: int = -1,
                     accumulate: int = ARF_ACC_F32, stream=None) -> None:
     """Reduced values of rows [row_begin, row_begin + row_count) into sums_out [T][H]."""
-    n, t, h = partials.shape
+    n, t, h = _partials(partials)
     _check(lib().arf_reduce_rows(_ptr(partials), n, t, row_begin, row_count, h,
                                  _dtype_code(partials), _dtype_code(sums_out), accumulate,
-                                 _ptr(sums_out), _stream(stream)), "arf_reduce_rows")
+                                 _dev("sums_out", sums_out, partials.device, t * h,
+                                      _act_dtypes()), _stream(stream)), "arf_reduce_rows")
 
 
 def arf_status_string(status: int) -> str:
@@ -178,18 +229,33 @@ def arf_set_path_override(path: int, waves_per_block: int = 0, chunks_per_lane: 
 
 
 def arf_e4m3_encode(x, out, stream=None) -> None:
-    _check(lib().arf_e4m3_encode(_ptr(x), _ptr(out), x.numel(), _stream(stream)),
-           "arf_e4m3_encode")
+    import torch
+    if x.device.type != "cuda":
+        raise ValueError("x must be a device tensor (got %s)" % x.device)
+    _check(lib().arf_e4m3_encode(_dev("x", x, x.device, None, (torch.float32,)),
+                                 _dev("out", out, x.device, x.numel(), (torch.uint8,)),
+                                 x.numel(), _stream(stream)), "arf_e4m3_encode")
+
+
+def _bytes_at_least(name, t, nbytes):
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor (got %s)" % (name, t.device))
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError("%s holds %d bytes; %d are accessed"
+                         % (name, t.numel() * t.element_size(), nbytes))
+    return _ptr(t)
 
 
 def arf_stream_copy(dst, src, nbytes: int | None = None, stream=None) -> None:
     nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
-    _check(lib().arf_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)),
+    _check(lib().arf_stream_copy(_bytes_at_least("dst", dst, nbytes),
+                                 _bytes_at_least("src", src, nbytes), nbytes, _stream(stream)),
            "arf_stream_copy")
 
 
 def arf_stream_mix(dst, write_bytes: int, src, read_bytes: int, units: int = 0,
                    stream=None) -> None:
-    _check(lib().arf_stream_mix(_ptr(dst) if write_bytes else None, write_bytes,
-                                _ptr(src) if read_bytes else None, read_bytes, units,
-                                _stream(stream)), "arf_stream_mix")
+    _check(lib().arf_stream_mix(_bytes_at_least("dst", dst, write_bytes) if write_bytes else None,
+                                write_bytes,
+                                _bytes_at_least("src", src, read_bytes) if read_bytes else None,
+                                read_bytes, units, _stream(stream)), "arf_stream_mix")

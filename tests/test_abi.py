@@ -232,3 +232,27 @@ def test_stream_mix_validation():
     assert L.arf_stream_mix(Q + 8, 32, P, 32, 0, None) == ALIGN
     assert L.arf_stream_mix(P + 16, 64, P, 64, 0, None) == ALIAS
     assert L.arf_stream_mix(Q, 16, P, 16, 2 ** 40, None) == SHAPE
+
+
+def test_binding_rejects_host_tensors_before_any_call():
+    # a host pointer handed to a kernel would fault the GPU: the binding refuses host
+    # tensors before it reaches the library
+    import torch
+    p = torch.zeros((2, 4, 64), dtype=torch.bfloat16)
+    r = torch.zeros((4, 64), dtype=torch.bfloat16)
+    g = torch.ones((64,), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        arf.arf_reduce_add_rmsnorm(p, r, g, 1e-6, residual_out=r)
+    with pytest.raises(ValueError, match="device tensor"):
+        arf.arf_reduce_add_rmsnorm_quant(p, r, g, 1e-6, torch.zeros((4, 64), dtype=torch.uint8),
+                                         arf.ARF_QUANT_PER_TOKEN)
+    with pytest.raises(ValueError, match="device tensor"):
+        arf.arf_fused_epilogue(p, r, g, 1e-6, norm_out=r)
+    with pytest.raises(ValueError, match="device tensor"):
+        arf.arf_reduce_rows(p, r)
+    with pytest.raises(ValueError, match=r"\[n_shards\]\[tokens\]\[hidden\]"):
+        arf.arf_reduce_rows(p[0], r)
+    with pytest.raises(ValueError, match="device tensor"):
+        arf.arf_e4m3_encode(torch.zeros(8), torch.zeros(8, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="device tensor"):
+        arf.arf_stream_copy(r, r)

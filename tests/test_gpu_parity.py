@@ -236,6 +236,25 @@ def test_every_shard_count(n):
     compare(run_gpu(pd_, rd, gd, w.eps, "bf16"), run_oracle(p, r, g, w.eps, "bf16", "bf16"))
 
 
+@pytest.mark.parametrize("pd,c", [("f32", 2), ("f32", 4), ("f32", 8), ("bf16", 8)])
+def test_eight_wave_geometry_every_shard_count(pd, c):
+    # the 8-wave geometry keeps 1 to 3 shards in flight depending on its load registers
+    # (16-byte pieces per lane: C for 16-bit partials, 2C for fp32); every shard count
+    # 1..16 runs through its prefetch ring, on a ragged row that fills all C chunks
+    h = 8 * 64 * 8 * c - 24
+    try:
+        arf.arf_set_path_override(2, 8, c)
+        for n in range(1, 17):
+            w = _case(n, 3, h, pd, "bf16", 500 + 17 * c + n, quant="per_token" if n % 2 else None)
+            say("8-wave geometry %s c=%d n=%d h=%d" % (pd, c, n, h))
+            (p, r, g), (pd_, rd, gd) = upload(w)
+            ref = run_oracle(p, r, g, w.eps, pd, "bf16", quant=w.quant)
+            got = run_gpu(pd_, rd, gd, w.eps, "bf16", quant=w.quant)
+            compare(got, ref, "%s c=%d n=%d" % (pd, c, n), min_exact=0.99)
+    finally:
+        arf.arf_set_path_override(0)
+
+
 def test_output_subsets_and_in_place():
     w = _case(4, 9, 4096, "bf16", "bf16", 11)
     (p, r, g), (pd_, rd, gd) = upload(w)
@@ -291,6 +310,36 @@ def test_rank_order_vector_on_gpu():
     g = torch.ones((h,), dtype=torch.bfloat16, device=DEV)
     got = run_gpu(p, r, g, 1e-6, "bf16")
     assert np.all(got["residual_out"] == 0x3F00)   # 0.5
+
+
+def test_binding_rejects_bad_tensors_and_launches_nothing():
+    say("binding argument checks")
+    w = _case(2, 4, 64, "bf16", "bf16", 5)
+    p, r, g = workloads.generate(w, DEV)
+    nout = Out((4, 64), torch.bfloat16)
+    bad = [
+        dict(residual_in=r.cpu()),                                          # host tensor
+        dict(norm_out=torch.empty((3, 64), dtype=torch.bfloat16, device=DEV)),   # short
+        dict(residual_out=torch.empty((4, 64), dtype=torch.float32, device=DEV)),  # dtype
+        dict(gamma=g[:32]),                                                 # short gamma
+    ]
+    for kw in bad:
+        args = dict(residual_in=r, gamma=g, norm_out=nout.t)
+        args.update(kw)
+        with pytest.raises((ValueError, TypeError)):
+            arf.arf_reduce_add_rmsnorm(p, args["residual_in"], args["gamma"], 1e-6,
+                                       residual_out=args.get("residual_out"),
+                                       norm_out=args["norm_out"])
+    q = torch.empty((4, 64), dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError):   # per-token scales for 3 of 4 rows
+        arf.arf_reduce_add_rmsnorm_quant(p, r, g, 1e-6, q, arf.ARF_QUANT_PER_TOKEN,
+                                         scale_out=torch.empty(3, device=DEV), norm_out=nout.t)
+    with pytest.raises(ValueError):   # MXFP4 codes sized for fp8
+        arf.arf_fused_epilogue(p, r, g, 1e-6, norm_out=nout.t, quant_out=q,
+                               mode=arf.ARF_QUANT_MXFP4,
+                               scale_out=torch.empty((4, 2), dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    assert bool((nout.raw == POISON)[: nout.nbytes].all()) and nout.canary_ok()
 
 
 def test_empty_call_writes_nothing():
