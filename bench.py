@@ -175,9 +175,11 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream(device=dev)
     t, h = w.tokens, w.hidden
-    run = Runner(w, dev, stream, sets=1)
-    ms_per_step, kernel_ms = run.measure(args.steps, args.warmup)
     B = w.algorithmic_bytes()
+    # workloads smaller than 1.5 GB rotate input/output sets so that the 256 MB Infinity
+    # Cache cannot serve a launch (c0-c2 still fit in it: see decode_cold for those)
+    run = Runner(w, dev, stream, sets=max(1, min(8, -(-1_500_000_000 // B))))
+    ms_per_step, kernel_ms = run.measure(args.steps, args.warmup)
     value = B / (ms_per_step * 1e-3) / 1e9
     achieved = B / (kernel_ms * 1e-3) / 1e9
     traffic = read_traffic(w.name)

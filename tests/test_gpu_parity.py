@@ -362,6 +362,59 @@ def test_repeat_runs_are_bit_identical():
         assert np.array_equal(a[k], b[k])
 
 
+
+def test_concurrent_calls_from_two_threads_on_two_streams():
+    # the library keeps no per-call state: two host threads enqueue calls with different
+    # shapes, types and modes on their own streams at the same time
+    import threading
+
+    cases = [_case(8, 128, 4096, "bf16", "bf16", 601),
+             _case(4, 96, 7168, "f32", "bf16", 602, quant="per_token")]
+    say("two threads, two streams")
+    work = []
+    for w in cases:
+        (p, r, g), (pd_, rd, gd) = upload(w)
+        ref = run_oracle(p, r, g, w.eps, w.partial_dtype, w.act_dtype, quant=w.quant)
+        t, h = w.tokens, w.hidden
+        outs = {"residual_out": Out((t, h), torch.bfloat16), "norm_out": Out((t, h), torch.bfloat16)}
+        if w.quant:
+            outs["quant_out"] = Out((t, h), torch.uint8)
+            outs["scale_out"] = Out((t,), torch.float32)
+        work.append((w, (pd_, rd, gd), outs, ref, torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    errors = []
+
+    def enqueue(w, ins, outs, stream):
+        try:
+            pd_, rd, gd = ins
+            for _ in range(25):
+                if w.quant:
+                    arf.arf_reduce_add_rmsnorm_quant(
+                        pd_, rd, gd, w.eps, outs["quant_out"].t, arf.ARF_QUANT_PER_TOKEN,
+                        scale_out=outs["scale_out"].t, residual_out=outs["residual_out"].t,
+                        norm_out=outs["norm_out"].t, stream=stream)
+                else:
+                    arf.arf_reduce_add_rmsnorm(pd_, rd, gd, w.eps,
+                                               residual_out=outs["residual_out"].t,
+                                               norm_out=outs["norm_out"].t, stream=stream)
+        except Exception as e:   # reported on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=enqueue, args=(w, ins, outs, st))
+               for w, ins, outs, _, st in work]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for w, _, outs, ref, _ in work:
+        got = {}
+        for k, o in outs.items():
+            assert o.canary_ok(), (w.name, k)
+            got[k] = o.t.cpu().numpy() if k in ("quant_out", "scale_out") else workloads.to_bits(o.t)
+        compare(got, ref, w.name)
+
 # ---- the quantiser's conversion and the copy probe -----------------------------------------
 
 def test_e4m3_conversion_matches_the_oracle():
