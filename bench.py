@@ -196,6 +196,7 @@ def main():
         steps2 = max(args.steps, 200)
         ms2, kms2 = run2.measure(steps2, max(args.warmup, 10))
         launch2 = percentiles_us(run2.distribution(steps2))
+        mix2 = None if args.no_copy_probe else mix_probe(w2, run2, stream)
         del run2
         torch.cuda.empty_cache()
         secondary = {"workload": w2.name, "buffer_sets": sets, "steps": steps2,
@@ -206,7 +207,10 @@ def main():
                      "tokens_per_s": round(w2.tokens / (kms2 * 1e-3), 1),
                      "plan": arf.arf_get_plan(w2.n_shards, w2.tokens, w2.hidden,
                                               {"bf16": 0, "f16": 1, "f32": 2}[w2.partial_dtype]),
-                     "traffic": read_traffic(w2.name)}
+                     "traffic": read_traffic(w2.name),
+                     "mix_GBs": mix2,
+                     "frac_of_mix_ceiling": None if mix2 is None else
+                                            round(B2 / (kms2 * 1e-3) / 1e9 / mix2, 4)}
 
     cpu = None
     parity = None
@@ -262,6 +266,34 @@ def main():
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def mix_probe(w, run, stream, reps=20):
+    """The workload's own read/write mix with no arithmetic (GB/s), rotating over the
+    runner's buffer sets like the timed launches: read a set's partials and write a
+    buffer of its own in the workload's write:read ratio, one unit per row (reads, then
+    writes, per unit)."""
+    import torch
+
+    import shard_reduce_residual_amd as arf
+
+    n, t, h = w.n_shards, w.tokens, w.hidden
+    B = w.algorithmic_bytes()
+    alg_read = n * t * h * w.sp + t * h * w.sa + h * w.sa + (4 if w.quant == "per_tensor" else 0)
+    read_b = n * t * h * w.sp
+    write_b = (int(read_b * (B - alg_read) / alg_read) // 16) * 16
+    outs = [torch.empty(write_b, dtype=torch.uint8, device=run.sets[0][0].device)
+            for _ in run.sets]
+    k = [0]
+
+    def one():
+        i = k[0] % len(run.sets)
+        k[0] += 1
+        arf.arf_stream_mix(outs[i], write_b, run.sets[i][0], read_b, units=t, stream=stream)
+
+    ms = _events_ms(one, stream, reps, 3)
+    del outs
+    return round((read_b + write_b) / (ms * 1e-3) / 1e9, 1)
 
 
 def hbm_probes(w, partials, stream, reps=10):
