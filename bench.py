@@ -160,8 +160,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU's share of the fused epilogue; runs on more than "
-              "one GPU are not part of this build (asked for --gpus %d, WORLD_SIZE %d)"
+        print("bench.py measures one GPU's share of the fused epilogue on one GPU; it has "
+              "no multi-GPU mode (asked for --gpus %d, WORLD_SIZE %d)"
               % (args.gpus, world), file=sys.stderr)
         return 2
 
