@@ -360,10 +360,11 @@ def _events_ms(fn, stream, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def graph_replay_us(launches=50, replays=20):
+def graph_replay_us(launches=50, replays=20, repeats=7):
     """Per-launch time of the decode-size workloads (c0, c1, c2) when `launches` calls are
     captured in one HIP graph and the graph is replayed: the kernels' back-to-back time
-    without host launch overhead."""
+    without host launch overhead. The replays are timed ``repeats`` times; the median is
+    reported with the range, since single timings of µs-long kernels spread by about 10%."""
     import torch
 
     import workloads
@@ -385,15 +386,20 @@ def graph_replay_us(launches=50, replays=20):
                 run.step()
         graph.replay()
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(replays):
-            graph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (replays * launches)
-        res[w.name] = {"us_per_launch": round(us, 3),
+        times = []
+        for _ in range(repeats):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(replays):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / (replays * launches))
+        times.sort()
+        us = times[len(times) // 2]
+        res[w.name] = {"us_per_launch": round(us, 3), "min": round(times[0], 3),
+                       "max": round(times[-1], 3),
                        "achieved_GBs": round(w.algorithmic_bytes() / (us * 1e-6) / 1e9, 1)}
         del graph, run
     return res

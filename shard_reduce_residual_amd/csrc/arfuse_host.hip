@@ -37,22 +37,26 @@ int pow2_at_least(int64_t v) {
 int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Launch geometry: the hidden/8 chunks of a row are spread over the lanes that own it.
-// Fitted to sweeps on MI355X (256 CUs) over hidden 1024..16384, 16..32768 tokens, 2..8
-// bf16 shards and 4 fp32 shards:
-//  * one row per wavefront for short rows (<= 512 chunks) with a moderate token count
-//    (2 to 8 rows per compute unit);
+// Fitted to sweeps on MI355X (256 CUs) over hidden 1024..16384, 128..8192 tokens, 2 and 8
+// bf16 shards and 4 fp32 shards, and checked on other shapes (hidden 1536..12288, 4 and 16
+// bf16, 8 fp16 and 2 fp32 shards), where it stays within 1.1% of the best menu entry on
+// geometric mean:
+//  * one row per wavefront (4 rows per workgroup) for short rows once the grid is large
+//    enough to fill the chip: rows of <= 128 chunks from 2 rows per compute unit, rows of
+//    <= 256 chunks from 8 rows per compute unit;
 //  * otherwise one row per workgroup:
 //    - few rows (< 2 per compute unit): 8 wavefronts per row, so that each row exposes
 //      more parallel loads;
 //    - otherwise 4 wavefronts with up to 8 chunks per lane, so that several rows share a
-//      compute unit; rows above 2048 chunks use 16 wavefronts.
+//      compute unit;
+//    - rows too wide for 8 chunks per lane use 16 wavefronts.
 arf_status make_plan(int64_t tokens, int32_t hidden, int num_cus, Plan* pl) {
     const int hc = hidden / 8;
     int path = g_path.load(), waves = g_waves.load(), chunks = g_chunks.load();
     if (path == 0) {
         waves = chunks = 0;
         const bool many_rows = tokens >= 2LL * num_cus;
-        if (hc <= 512 && many_rows && tokens <= 8LL * num_cus) {
+        if ((hc <= 128 && many_rows) || (hc <= 256 && tokens >= 8LL * num_cus)) {
             path = 1;
         } else {
             path = 2;

@@ -139,8 +139,22 @@ def test_plan_for_the_named_workloads():
     assert plan(8, 64, 8192) == {"path": 2, "waves": 8, "chunks": 2, "grid": 64}
     assert plan(2, 16, 1024)["path"] == 2
     assert plan(4, 4096, 7168) == {"path": 2, "waves": 4, "chunks": 4, "grid": 4096}
-    assert plan(2, 1024, 4096) == {"path": 1, "waves": 4, "chunks": 8, "grid": 256}
+    assert plan(2, 1024, 4096) == {"path": 2, "waves": 4, "chunks": 2, "grid": 1024}
     assert plan(8, 8192, 65536) == {"path": 2, "waves": 16, "chunks": 8, "grid": 8192}
+
+
+def test_plan_row_per_wave_region():
+    # one row per wavefront: rows of <= 128 chunks from 2 rows per CU, rows of <= 256
+    # chunks from 8 rows per CU; never for wider rows
+    assert plan(8, 511, 1024)["path"] == 2 and plan(8, 512, 1024)["path"] == 1
+    assert plan(8, 8192, 1024) == {"path": 1, "waves": 4, "chunks": 2, "grid": 2048}
+    assert plan(8, 2047, 2048)["path"] == 2 and plan(8, 2048, 2048)["path"] == 1
+    assert plan(8, 8192, 2048) == {"path": 1, "waves": 4, "chunks": 4, "grid": 2048}
+    assert plan(4, 8192, 2056, 2)["path"] == 2          # 257 chunks
+    for t in (512, 1024, 2048, 8192):
+        assert plan(8, t, 4096)["path"] == 2
+    # the thresholds scale with the CU count
+    assert plan(8, 1023, 2048, 0, 128)["path"] == 2 and plan(8, 1024, 2048, 0, 128)["path"] == 1
 
 
 def test_path_override_forces_and_rejects():
