@@ -49,8 +49,10 @@ def torch_bf16_bits(x_f32):
 
 
 def numpy_f16_bits(x):
-    """fp32 or fp64 -> binary16 by numpy's cast (round to nearest even, one rounding)."""
-    return np.asarray(x).astype(np.float16).view(np.uint16)
+    """fp32 or fp64 -> binary16 by numpy's cast (round to nearest even, one rounding;
+    overflow to +-inf is intended, so numpy's overflow warning is silenced)."""
+    with np.errstate(over="ignore", invalid="ignore"):
+        return np.asarray(x).astype(np.float16).view(np.uint16)
 
 
 def bf16_bits_to_f64(b):
@@ -101,7 +103,8 @@ _E4M3 = e4m3_values()
 def e4m3_brute(x):
     """Nearest finite E4M3 value, ties to the even code, saturating at 448; +-inf -> +-448;
     NaN -> S.1111.111. Sign is kept (tiny negatives give -0 = 0x80)."""
-    x = np.asarray(x, dtype=np.float32).astype(np.float64).ravel()
+    with np.errstate(over="ignore", invalid="ignore"):   # inf and NaN inputs are intended
+        x = np.asarray(x, dtype=np.float32).astype(np.float64).ravel()
     out = np.empty(x.size, np.uint8)
     for s in range(0, x.size, 65536):
         xs = x[s:s + 65536]
