@@ -201,6 +201,40 @@ def test_sweep_shapes_auto_path(pd, ad):
         compare(got, ref, "n=%d t=%d h=%d" % (n, t, h), min_exact=0.99)
 
 
+XN = (1, 2, 3, 4, 7, 8, 16)
+XT = (1, 2, 3, 17, 64)
+XH = (8, 16, 64, 264, 1024, 2048, 4096, 7168, 8192, 16384)
+
+
+@pytest.mark.parametrize("pd,ad", [("bf16", "bf16"), ("f16", "f16"), ("f32", "bf16"),
+                                   ("f32", "f16")])
+def test_cross_product_sweep_both_paths(pd, ad):
+    # N x T x H over small token counts, per-token fp8 on every other case, each case on
+    # the planned geometry and again with the other path forced (one row per wavefront
+    # only where a wavefront covers the row); every fourth case in place
+    for n in XN:
+        for t in XT:
+            for h in XH:
+                quant = "per_token" if (n + t) % 2 else None
+                w = _case(n, t, h, pd, ad, 7000 + 100 * n + t, quant=quant)
+                (p, r, g), (pd_, rd, gd) = upload(w)
+                ref = run_oracle(p, r, g, w.eps, pd, ad, quant=quant)
+                auto = arf.arf_get_plan(n, t, h, {"bf16": 0, "f16": 1, "f32": 2}[pd])["path"]
+                other = 2 if auto == 1 else (1 if h <= 4096 else None)
+                in_place = (n + t + h // 8) % 4 == 0
+                for forced in (0, other):
+                    if forced is None:
+                        continue
+                    say("cross n=%d t=%d h=%d %s/%s quant=%s path=%s in_place=%s"
+                        % (n, t, h, pd, ad, quant, forced or "auto", in_place))
+                    try:
+                        arf.arf_set_path_override(forced)
+                        got = run_gpu(pd_, rd, gd, w.eps, ad, quant=quant, in_place=in_place)
+                    finally:
+                        arf.arf_set_path_override(0)
+                    compare(got, ref, "n=%d t=%d h=%d path=%s" % (n, t, h, forced or "auto"),
+                            min_exact=0.99)
+
 def _geometries(h):
     hc = h // 8
     out = []
