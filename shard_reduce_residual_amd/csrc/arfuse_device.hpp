@@ -327,6 +327,11 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
     const auto r_out = make_rsrc((char*)p.residual_out + act_off, p.residual_out ? act_row : 0u);
     const auto y_out = make_rsrc((char*)p.norm_out + act_off, p.norm_out ? act_row : 0u);
     const auto g_in = make_rsrc(p.gamma, act_row);
+    // The per-tensor scale is read before any store: read after the output stores, its
+    // load waited for all of them to complete (one memory counter covers loads and
+    // stores) and then for its own round trip, on the critical path of short launches.
+    // It cannot alias an output (the host rejects that overlap).
+    const float scale_tensor = p.quant_mode == kQuantTensor ? p.scale_in[0] : 0.0f;
 
     __amdgpu_buffer_rsrc_t part[N];
 #pragma unroll
@@ -475,7 +480,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
         scale = amax / 448.0f;
         if (gl == 0) static_cast<float*>(p.scale_out)[row] = scale;
     } else {
-        scale = p.scale_in[0];
+        scale = scale_tensor;
     }
     const float inv_scale = scale > 0.0f ? 1.0f / scale : 0.0f;
     const auto q_out = make_rsrc(p.quant_out + row * (int64_t)H, H);
