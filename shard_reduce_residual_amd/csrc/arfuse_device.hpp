@@ -19,8 +19,8 @@
 //  * Streaming data (partials, residual, outputs) carries the non-temporal hint; gamma is
 //    shared by all rows and uses the default policy.
 //  * The mean of squares is accumulated in fp64 per lane (squares of 16-bit values are
-//    exact in fp64), reduced across the wavefront with cross-lane shuffles and across
-//    wavefronts through LDS in a fixed order, so the result does not depend on timing.
+//    exact in fp64), reduced across the wavefront with DPP lane moves and readlane, and
+//    across wavefronts through LDS, in a fixed order: the result does not depend on timing.
 //  * The normalised row stays in registers (packed 16-bit) between the two reductions of
 //    the per-token fp8 scale, so nothing is re-read from HBM.
 #pragma once
@@ -155,16 +155,60 @@ __device__ __forceinline__ uint32_t e2m1_code(float v) {
 
 // ---- cross-lane reductions (wave64) ------------------------------------------------------
 
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
+// Data-parallel-primitive (DPP) lane moves: a VALU operand modifier, no LDS round trip.
+// Within each row of 16 lanes: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1]
+// (lane ^ 2), row_half_mirror (lane i <-> 7 - i in each group of 8), row_mirror (lane i <->
+// 15 - i in each row). After xor-1, xor-2 and half-mirror steps every lane of a group of 8
+// holds the same combination of the group's values; after row_mirror, of the row's.
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double readlane(double v, int lane) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the 64 lanes: a DPP butterfly inside each row of 16 (every lane of a row ends
+// with the same value, since each step adds the same two operands in either order), then
+// the four row sums in a fixed order. The result is the same in every lane and on every
+// run.
+__device__ __forceinline__ double wave_sum(double v) {
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    v += dpp<kDppMirror>(v);
+    return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
+}
+
+// Maximum over the 64 lanes (fmaxf: a NaN operand is skipped), the same pattern.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp<kDppMirror>(v));
+    const float a = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)),
+                          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16)));
+    const float b = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32)),
+                          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48)));
+    return fmaxf(a, b);
 }
 
 // ---- the fused kernel -------------------------------------------------------------------
@@ -251,9 +295,9 @@ struct Layout {
                 float a = 0.0f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) a = fmaxf(a, __builtin_fabsf(y[4 * w + e]));
-                a = fmaxf(a, __shfl_xor(a, 1, 64));
-                a = fmaxf(a, __shfl_xor(a, 2, 64));
-                a = fmaxf(a, __shfl_xor(a, 4, 64));
+                a = fmaxf(a, dpp<kDppXor1>(a));   // the 8 lanes of the block
+                a = fmaxf(a, dpp<kDppXor2>(a));
+                a = fmaxf(a, dpp<kDppHalfMirror>(a));
                 const uint32_t code = mx_scale_code(a);
                 const float inv = __builtin_amdgcn_ldexpf(1.0f, 127 - (int)code);
                 uint32_t packed = 0;
@@ -270,8 +314,8 @@ struct Layout {
             float a = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) a = fmaxf(a, __builtin_fabsf(y[e]));
-            a = fmaxf(a, __shfl_xor(a, 1, 64));
-            a = fmaxf(a, __shfl_xor(a, 2, 64));
+            a = fmaxf(a, dpp<kDppXor1>(a));   // the 4 lanes of the block
+            a = fmaxf(a, dpp<kDppXor2>(a));
             const uint32_t code = mx_scale_code(a);
             const float inv = __builtin_amdgcn_ldexpf(1.0f, 127 - (int)code);
             uint32_t packed = 0;
