@@ -314,7 +314,11 @@ def hbm_probes(w, partials, stream, reps=10):
     mix_write = (int(read_b * alg_write / alg_read) // 16) * 16
     one_gib = 1 << 30
     dst = torch.empty(max(mix_write, one_gib), dtype=torch.uint8, device=dev)
-    src2 = partials.view(torch.uint8).view(-1)[:one_gib]
+    flat = partials.view(torch.uint8).view(-1)
+    # the copy probe moves 1 GiB: from the partials when they are that large, else from a
+    # buffer of its own (its contents do not matter)
+    src2 = (flat[:one_gib] if flat.numel() >= one_gib
+            else torch.empty(one_gib, dtype=torch.uint8, device=dev))
 
     def timed(fn):
         fn()
