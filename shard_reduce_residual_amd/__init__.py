@@ -78,12 +78,29 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
+_T = None
+
+
+def _types():
+    """torch dtypes used by the checks, resolved once (torch is imported lazily)."""
+    global _T
+    if _T is None:
+        import torch
+
+        class _Types:
+            codes = {torch.bfloat16: ARF_BF16, torch.float16: ARF_F16, torch.float32: ARF_F32}
+            act = (torch.bfloat16, torch.float16)
+            f32 = (torch.float32,)
+            u8 = (torch.uint8,)
+        _T = _Types
+    return _T
+
+
 def _dtype_code(t) -> int:
-    import torch
-    codes = {torch.bfloat16: ARF_BF16, torch.float16: ARF_F16, torch.float32: ARF_F32}
-    if t.dtype not in codes:
+    code = _types().codes.get(t.dtype)
+    if code is None:
         raise TypeError("unsupported dtype %s" % t.dtype)
-    return codes[t.dtype]
+    return code
 
 
 def _ptr(t):
@@ -94,33 +111,34 @@ def _ptr(t):
     return t.data_ptr()
 
 
-def _dev(name, t, device, numel=None, dtypes=None):
+def _dev(name, t, dev, numel=None, dtypes=None):
     """Device pointer of ``t`` after the checks the C ABI cannot make: a contiguous tensor
-    on ``device`` (a host pointer handed to a kernel would fault the GPU), with ``numel``
-    elements of one of ``dtypes`` (a short buffer would be written past its end). None
-    stays None (an optional buffer left out)."""
+    on device index ``dev`` (a host pointer handed to a kernel would fault the GPU), with
+    ``numel`` elements of one of ``dtypes`` (a short buffer would be written past its end).
+    None stays None (an optional buffer left out)."""
     if t is None:
         return None
-    if t.device != device:
-        raise ValueError("%s is on %s; the call runs on %s" % (name, t.device, device))
+    if (t.get_device() == dev and (numel is None or t.numel() == numel)
+            and (dtypes is None or t.dtype in dtypes) and t.is_contiguous()):
+        return t.data_ptr()
+    if t.get_device() != dev:
+        raise ValueError("%s is on %s; the call runs on cuda:%d" % (name, t.device, dev))
     if dtypes is not None and t.dtype not in dtypes:
         raise TypeError("%s has dtype %s; expected %s" % (name, t.dtype, dtypes))
     if numel is not None and t.numel() != numel:
         raise ValueError("%s has %d elements; expected %d" % (name, t.numel(), numel))
-    return _ptr(t)
+    raise ValueError("%s must be contiguous" % name)
 
 
 def _partials(partials):
+    """(n_shards, tokens, hidden, device index) of a [N][T][H] device tensor."""
+    dev = partials.get_device()
     if partials.dim() != 3:
         raise ValueError("partials must be [n_shards][tokens][hidden]")
-    if partials.device.type != "cuda":
+    if dev < 0:
         raise ValueError("partials must be a device tensor (got %s)" % partials.device)
-    return partials.shape
-
-
-def _act_dtypes():
-    import torch
-    return (torch.bfloat16, torch.float16)
+    n, t, h = partials.shape
+    return n, t, h, dev
 
 
 def _stream(stream):
@@ -141,11 +159,11 @@ def arf_reduce_add_rmsnorm(partials, residual_in, gamma, eps: float, residual_ou
                            norm_out=None, stream=None) -> None:
     """partials [N][T][H] (bf16/f16, or f32); residual_in/_out, norm_out [T][H] and
     gamma [H] in the activation type. Enqueues one kernel on ``stream``."""
-    n, t, h = _partials(partials)
-    dev, act = partials.device, (residual_in.dtype,)
+    n, t, h, dev = _partials(partials)
+    act = (residual_in.dtype,)
     st = lib().arf_reduce_add_rmsnorm(_ptr(partials), n, t, h, _dtype_code(partials),
                                       _dtype_code(residual_in),
-                                      _dev("residual_in", residual_in, dev, t * h, _act_dtypes()),
+                                      _dev("residual_in", residual_in, dev, t * h, _types().act),
                                       _dev("residual_out", residual_out, dev, t * h, act),
                                       _dev("gamma", gamma, dev, h, act), float(eps),
                                       _dev("norm_out", norm_out, dev, t * h, act),
@@ -159,18 +177,17 @@ def arf_reduce_add_rmsnorm_quant(partials, residual_in, gamma, eps: float, quant
     """As arf_reduce_add_rmsnorm plus ``quant_out`` [T][H] uint8 E4M3 codes;
     ``mode`` ARF_QUANT_PER_TENSOR (``scale_in``: 1-element f32 device tensor) or
     ARF_QUANT_PER_TOKEN (``scale_out``: [T] f32 device tensor, written)."""
-    import torch
-    n, t, h = _partials(partials)
-    dev, act = partials.device, (residual_in.dtype,)
+    n, t, h, dev = _partials(partials)
+    act, T = (residual_in.dtype,), _types()
     st = lib().arf_reduce_add_rmsnorm_quant(
         _ptr(partials), n, t, h, _dtype_code(partials), _dtype_code(residual_in),
-        _dev("residual_in", residual_in, dev, t * h, _act_dtypes()),
+        _dev("residual_in", residual_in, dev, t * h, T.act),
         _dev("residual_out", residual_out, dev, t * h, act),
         _dev("gamma", gamma, dev, h, act), float(eps),
         _dev("norm_out", norm_out, dev, t * h, act),
-        _dev("quant_out", quant_out, dev, t * h, (torch.uint8,)), int(mode),
-        _dev("scale_in", scale_in, dev, 1, (torch.float32,)),
-        _dev("scale_out", scale_out, dev, t, (torch.float32,)), _stream(stream))
+        _dev("quant_out", quant_out, dev, t * h, T.u8), int(mode),
+        _dev("scale_in", scale_in, dev, 1, T.f32),
+        _dev("scale_out", scale_out, dev, t, T.f32), _stream(stream))
     _check(st, "arf_reduce_add_rmsnorm_quant")
 
 
@@ -179,32 +196,30 @@ def arf_fused_epilogue(partials, residual_in, gamma, eps: float, residual_out=No
                        scale_in=None, scale_out=None, accumulate: int = ARF_ACC_F32,
                        row_begin: int = 0, row_count: int = -1, stream=None) -> None:
     """The general call: row range and accumulation mode (see arf_params)."""
-    import torch
-    n, t, h = _partials(partials)
-    dev, act = partials.device, (residual_in.dtype,)
+    n, t, h, dev = _partials(partials)
+    act, T = (residual_in.dtype,), _types()
     mx = quant_out is not None and mode == ARF_QUANT_MXFP4
     a = arf_params(ctypes.sizeof(arf_params), n, _ptr(partials), t, row_begin, row_count, h,
                    _dtype_code(partials), _dtype_code(residual_in), accumulate,
-                   _dev("residual_in", residual_in, dev, t * h, _act_dtypes()),
+                   _dev("residual_in", residual_in, dev, t * h, T.act),
                    _dev("residual_out", residual_out, dev, t * h, act),
                    _dev("gamma", gamma, dev, h, act), float(eps),
                    _dev("norm_out", norm_out, dev, t * h, act),
-                   _dev("quant_out", quant_out, dev, t * h // 2 if mx else t * h,
-                        (torch.uint8,)), mode,
-                   _dev("scale_in", scale_in, dev, 1, (torch.float32,)),
+                   _dev("quant_out", quant_out, dev, t * h // 2 if mx else t * h, T.u8), mode,
+                   _dev("scale_in", scale_in, dev, 1, T.f32),
                    _dev("scale_out", scale_out, dev, t * h // 32 if mx else t,
-                        (torch.uint8,) if mx else (torch.float32,)))
+                        T.u8 if mx else T.f32))
     _check(lib().arf_fused_epilogue(ctypes.byref(a), _stream(stream)), "arf_fused_epilogue")
 
 
 def arf_reduce_rows(partials, sums_out, row_begin: int = 0, row_count: int = -1,
                     accumulate: int = ARF_ACC_F32, stream=None) -> None:
     """Reduced values of rows [row_begin, row_begin + row_count) into sums_out [T][H]."""
-    n, t, h = _partials(partials)
+    n, t, h, dev = _partials(partials)
     _check(lib().arf_reduce_rows(_ptr(partials), n, t, row_begin, row_count, h,
                                  _dtype_code(partials), _dtype_code(sums_out), accumulate,
-                                 _dev("sums_out", sums_out, partials.device, t * h,
-                                      _act_dtypes()), _stream(stream)), "arf_reduce_rows")
+                                 _dev("sums_out", sums_out, dev, t * h, _types().act),
+                                 _stream(stream)), "arf_reduce_rows")
 
 
 def arf_status_string(status: int) -> str:
@@ -229,16 +244,16 @@ def arf_set_path_override(path: int, waves_per_block: int = 0, chunks_per_lane: 
 
 
 def arf_e4m3_encode(x, out, stream=None) -> None:
-    import torch
-    if x.device.type != "cuda":
+    dev = x.get_device()
+    if dev < 0:
         raise ValueError("x must be a device tensor (got %s)" % x.device)
-    _check(lib().arf_e4m3_encode(_dev("x", x, x.device, None, (torch.float32,)),
-                                 _dev("out", out, x.device, x.numel(), (torch.uint8,)),
+    _check(lib().arf_e4m3_encode(_dev("x", x, dev, None, _types().f32),
+                                 _dev("out", out, dev, x.numel(), _types().u8),
                                  x.numel(), _stream(stream)), "arf_e4m3_encode")
 
 
 def _bytes_at_least(name, t, nbytes):
-    if t.device.type != "cuda":
+    if t.get_device() < 0:
         raise ValueError("%s must be a device tensor (got %s)" % (name, t.device))
     if t.numel() * t.element_size() < nbytes:
         raise ValueError("%s holds %d bytes; %d are accessed"
