@@ -125,6 +125,14 @@ def upload(w):
     return (p, r, g), (p.to(DEV), r.to(DEV), g.to(DEV))
 
 
+def test_inputs_are_the_same_on_the_gpu_and_the_cpu():
+    # the counter-based generator gives the same bits on either device
+    for key in ("c0", "c1", "c2", "c3"):
+        w = workloads.WORKLOADS[key]
+        say("generator %s cpu vs gpu" % w.name)
+        for a, b in zip(workloads.generate(w, "cpu"), workloads.generate(w, DEV)):
+            assert torch.equal(a, b.cpu()), w.name
+
 # ---- the five workloads --------------------------------------------------------------------
 
 @pytest.mark.parametrize("key", ["c0", "c1", "c2", "c3"])

@@ -4,18 +4,21 @@ This module holds shapes, value distributions and random draws only: none of the
 method's arithmetic. Both the oracle side and the HIP side receive exactly the arrays
 produced here.
 
+Random numbers come from a counter-based generator, so that any element can be drawn on
+its own and the values are the same on the CPU and on the GPU: element n of stream s is
+the SplitMix64 output function (Steele, Lea and Flood, "Fast splittable pseudorandom
+number generators", OOPSLA 2014) applied to seed + phi * (c + 1), with c = (s << 40) | n
+and phi = 0x9E3779B97F4A7C15, all modulo 2^64.
+  * uniform u = (x >> 11) * 2^-53, in [0, 1);
+  * normal: Box-Muller on the pairs (2k, 2k+1) in fp64, r = sqrt(-2 ln(1 - u_2k)),
+    z_2k = r cos(2 pi u_2k+1), z_2k+1 = r sin(2 pi u_2k+1).
 Recipe (each workload is one of the five named below):
-  * partials  [N][T][H]: normal(0, std) drawn in fp32, then cast (round-to-nearest-even,
-    torch's own cast) to the partial type. With outliers, a seeded choice of
-    round(outlier_frac * H) hidden channels is multiplied by ``outlier_scale`` in fp32 in
-    every shard and token before the cast.
-  * residual  [T][H]: normal(0, residual_std) in fp32, cast to the activation type.
-  * gamma     [H]:    uniform(0.5, 1.5) in fp32, cast to the activation type.
-Each of the four draws uses its own torch.Generator seeded with seed*16 + stream
-(stream 0 partials, 1 residual, 2 gamma, 3 outlier channels). The outlier channel choice
-always uses a CPU generator. For a given (workload, device type) the values are
-reproducible; CPU and GPU generators produce different streams, so a test that checks a
-GPU run copies the generated inputs to the host for the oracle.
+  * partials  [N][T][H]: stream 0 over the flattened array, normal(0, std) in fp64. With
+    outliers, round(outlier_frac * H) hidden channels (stream 3: a partial Fisher-Yates
+    shuffle of 0..H-1) are multiplied by ``outlier_scale`` in fp64 in every shard and
+    token. Then rounded to fp32 and, for 16-bit partials, from fp32 to the partial type.
+  * residual  [T][H]: stream 1, normal(0, residual_std), cast the same way.
+  * gamma     [H]:    stream 2, 0.5 + u, cast the same way.
 """
 from __future__ import annotations
 
@@ -87,41 +90,90 @@ WORKLOADS = {
 }
 
 
-def _gen(seed: int, stream: int, device) -> torch.Generator:
-    g = torch.Generator(device=device)
-    g.manual_seed(seed * 16 + stream)
-    return g
+_PHI = 0x9E3779B97F4A7C15
+_MIX1 = 0xBF58476D1CE4E5B9
+_MIX2 = 0x94D049BB133111EB
+_MASK64 = (1 << 64) - 1
+
+
+def _signed(u: int) -> int:
+    """A 64-bit pattern as the int64 value with the same bits."""
+    return u - (1 << 64) if u >= 1 << 63 else u
+
+
+def _srl(x: torch.Tensor, k: int) -> torch.Tensor:
+    """Logical right shift of int64 bit patterns (torch's >> is arithmetic)."""
+    return (x >> k) & ((1 << (64 - k)) - 1)
+
+
+def raw64(seed: int, stream: int, start: int, count: int, device) -> torch.Tensor:
+    """Elements start .. start+count-1 of a stream, as int64 bit patterns. int64 products
+    wrap modulo 2^64 on both devices, which is the generator's arithmetic."""
+    c = torch.arange(start, start + count, dtype=torch.int64, device=device) | (stream << 40)
+    z = (c + 1) * _signed(_PHI) + _signed(seed & _MASK64)
+    z = (z ^ _srl(z, 30)) * _signed(_MIX1)
+    z = (z ^ _srl(z, 27)) * _signed(_MIX2)
+    return z ^ _srl(z, 31)
+
+
+def raw64_reference(seed: int, stream: int, n: int) -> int:
+    """One element with Python integers, for checking raw64."""
+    z = (seed + _PHI * (((stream << 40) | n) + 1)) & _MASK64
+    z = ((z ^ (z >> 30)) * _MIX1) & _MASK64
+    z = ((z ^ (z >> 27)) * _MIX2) & _MASK64
+    return z ^ (z >> 31)
+
+
+def uniform(seed: int, stream: int, start: int, count: int, device) -> torch.Tensor:
+    """fp64 uniforms in [0, 1)."""
+    return _srl(raw64(seed, stream, start, count, device), 11).to(torch.float64) * 2.0 ** -53
+
+
+def normal(seed: int, stream: int, start: int, count: int, device) -> torch.Tensor:
+    """fp64 standard normals; start and count are even (Box-Muller pairs)."""
+    assert start % 2 == 0 and count % 2 == 0
+    u = uniform(seed, stream, start, count, device).view(-1, 2)
+    r = torch.sqrt(-2.0 * torch.log(1.0 - u[:, 0]))
+    t = (2.0 * math.pi) * u[:, 1]
+    return torch.stack((r * torch.cos(t), r * torch.sin(t)), dim=1).view(-1)
 
 
 def outlier_channels(w: Workload) -> torch.Tensor:
-    """Sorted indices of the hidden channels that carry outliers (CPU int64)."""
+    """Sorted indices of the hidden channels that carry outliers (CPU int64): the first
+    round(outlier_frac * H) entries of a Fisher-Yates shuffle of 0..H-1 drawn from
+    stream 3."""
     k = int(round(w.outlier_frac * w.hidden))
     if k == 0:
         return torch.empty(0, dtype=torch.int64)
-    perm = torch.randperm(w.hidden, generator=_gen(w.seed, 3, "cpu"))
-    return torch.sort(perm[:k]).values
+    perm = list(range(w.hidden))
+    draws = raw64(w.seed, 3, 0, k, "cpu").tolist()
+    for i in range(k):
+        j = i + (draws[i] & _MASK64) % (w.hidden - i)
+        perm[i], perm[j] = perm[j], perm[i]
+    return torch.sort(torch.tensor(perm[:k], dtype=torch.int64)).values
+
+
+def _store(x64: torch.Tensor, dtype) -> torch.Tensor:
+    x = x64.to(torch.float32)
+    return x if dtype == torch.float32 else x.to(dtype)
 
 
 def generate(w: Workload, device="cpu"):
     """Return (partials [N][T][H], residual [T][H], gamma [H]) as torch tensors on
-    ``device`` in the workload's types."""
+    ``device`` in the workload's types; the same values on every device."""
     device = torch.device(device)
     pdt, adt = TORCH_DTYPES[w.partial_dtype], TORCH_DTYPES[w.act_dtype]
     n, t, h = w.n_shards, w.tokens, w.hidden
-    gp = _gen(w.seed, 0, device)
     partials = torch.empty((n, t, h), dtype=pdt, device=device)
     cols = outlier_channels(w).to(device)
-    for r in range(n):  # one shard at a time bounds the fp32 temporary
-        x = torch.randn((t, h), generator=gp, device=device, dtype=torch.float32)
-        x.mul_(w.partial_std)
+    for r in range(n):  # one shard at a time bounds the fp64 temporaries
+        x = normal(w.seed, 0, r * t * h, t * h, device).view(t, h).mul_(w.partial_std)
         if cols.numel():
             x[:, cols] *= w.outlier_scale
-        partials[r].copy_(x)
+        partials[r].copy_(_store(x, pdt))
         del x
-    res = torch.randn((t, h), generator=_gen(w.seed, 1, device), device=device,
-                      dtype=torch.float32).mul_(w.residual_std).to(adt)
-    gamma = (torch.rand((h,), generator=_gen(w.seed, 2, device), device=device,
-                        dtype=torch.float32) + 0.5).to(adt)
+    res = _store(normal(w.seed, 1, 0, t * h, device).view(t, h) * w.residual_std, adt)
+    gamma = _store(uniform(w.seed, 2, 0, h, device) + 0.5, adt)
     return partials, res, gamma
 
 
