@@ -257,6 +257,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "hbm_probes": probes,
+        "frac_of_copy_ceiling": None if probes is None else round(achieved / probes["copy_GBs"], 4),
         "frac_of_mix_ceiling": None if probes is None else round(achieved / probes["mix_GBs"], 4),
         "secondary": secondary,
         "variants": variants,
