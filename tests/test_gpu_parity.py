@@ -801,3 +801,107 @@ def test_special_values_match_the_oracle(value):
     assert np.array_equal(qg[~nan_codes], qr[~nan_codes])
     sg, sr = got["scale_out"], ref["scale_out"]
     assert np.array_equal(np.isnan(sg), np.isnan(sr)) and np.array_equal(sg[~np.isnan(sr)], sr[~np.isnan(sr)])
+
+
+# ---- seeded random general calls -------------------------------------------------------------
+
+def _random_case(rng, k):
+    """One general call: sizes, types, accumulation, row range, output subset, in place,
+    quantised copy and eps, drawn from a fixed-seed generator."""
+    pd, ad = [("bf16", "bf16"), ("f16", "f16"), ("f32", "bf16"), ("f32", "f16")][rng.integers(4)]
+    n = int(rng.integers(1, 17))
+    t = int(rng.choice([0, 1, 2, 3, 5, 17, 64, 130, 300]))
+    h = 8 * int(np.exp(rng.uniform(0.0, np.log(2500.0))))
+    quant = [None, "per_tensor", "per_token", "mxfp4"][rng.integers(4)]
+    if quant == "mxfp4":
+        h = -(-h // 32) * 32
+    while n * t * h > (1 << 22):   # bound the case's size
+        t //= 2
+    res, norm = bool(rng.random() < 0.8), bool(rng.random() < 0.8)
+    if quant is None and not (res or norm):
+        norm = True
+    begin = int(rng.integers(0, t + 1))
+    count = int(rng.integers(-1, t - begin + 1))
+    return dict(n=n, t=t, h=h, pd=pd, ad=ad, quant=quant, res=res, norm=norm,
+                in_place=res and bool(rng.random() < 0.3), begin=begin, count=count,
+                acc=["f32", "partial"][rng.integers(2)],
+                eps=float(rng.choice([0.0, 1e-6, 1e-5, 0.1])),
+                scale=float(rng.uniform(1e-3, 0.1)), seed=9000 + k)
+
+
+def test_seeded_random_general_calls_match_the_oracle():
+    rng = np.random.default_rng(20261202)
+    for k in range(200):
+        c = _random_case(rng, k)
+        w = _case(c["n"], c["t"], c["h"], c["pd"], c["ad"], c["seed"], eps=c["eps"])
+        say("random call %d: %s" % (k, c))
+        (p, r, g), (pd_, rd, gd) = upload(w)
+        t, h, adt = c["t"], c["h"], TORCH[c["ad"]]
+        rows = slice(c["begin"], t if c["count"] < 0 else c["begin"] + c["count"])
+        # GPU: every output poisoned and guarded; in place writes the residual over a copy
+        rin = rd.clone() if c["in_place"] else rd
+        rout = None if (not c["res"] or c["in_place"]) else Out((t, h), adt)
+        nout = Out((t, h), adt) if c["norm"] else None
+        q = sout = None
+        sin = None
+        kw = {}
+        if c["quant"] == "mxfp4":
+            q, sout = Out((t, h // 2), torch.uint8), Out((t, h // 32), torch.uint8)
+            kw = dict(quant_out=q.t, mode=arf.ARF_QUANT_MXFP4, scale_out=sout.t)
+        elif c["quant"] == "per_token":
+            q, sout = Out((t, h), torch.uint8), Out((t,), torch.float32)
+            kw = dict(quant_out=q.t, mode=arf.ARF_QUANT_PER_TOKEN, scale_out=sout.t)
+        elif c["quant"] == "per_tensor":
+            q = Out((t, h), torch.uint8)
+            sin = torch.tensor([c["scale"]], dtype=torch.float32, device=DEV)
+            kw = dict(quant_out=q.t, mode=arf.ARF_QUANT_PER_TENSOR, scale_in=sin)
+        arf.arf_fused_epilogue(pd_, rin, gd, w.eps,
+                               residual_out=rin if c["in_place"] else (rout.t if rout else None),
+                               norm_out=nout.t if nout else None, row_begin=c["begin"],
+                               row_count=c["count"],
+                               accumulate=arf.ARF_ACC_PARTIAL if c["acc"] == "partial" else arf.ARF_ACC_F32,
+                               **kw)
+        torch.cuda.synchronize()
+        # oracle: the same call, unwritten rows left at the poison byte
+        rb = workloads.to_bits(r)
+        ref = oracle.reduce_add_rmsnorm(
+            workloads.to_bits(p), rb.copy() if c["in_place"] else rb, workloads.to_bits(g),
+            w.eps, partial_dtype=c["pd"], act_dtype=c["ad"],
+            residual_out=c["res"], norm_out=c["norm"], quant=c["quant"],
+            scale_in=c["scale"] if c["quant"] == "per_tensor" else None,
+            residual_out_array=None, accumulate=c["acc"], rows=(c["begin"], c["count"]),
+            out_init=POISON, n_threads=THREADS)
+        if c["in_place"]:
+            exp = rb.copy()
+            exp[rows] = oracle.reduce_add_rmsnorm(
+                workloads.to_bits(p), rb, workloads.to_bits(g), w.eps, partial_dtype=c["pd"],
+                act_dtype=c["ad"], norm_out=False, accumulate=c["acc"],
+                rows=(c["begin"], c["count"]), n_threads=THREADS)["residual_out"][rows]
+            assert np.array_equal(workloads.to_bits(rin), exp), k
+        got = {}
+        for name, o in (("residual_out", rout), ("norm_out", nout), ("quant_out", q),
+                        ("scale_out", sout)):
+            if o is None:
+                continue
+            assert o.canary_ok(), (k, name)
+            got[name] = workloads.to_bits(o.t) if o.t.dtype in (torch.bfloat16, torch.float16) \
+                else o.t.cpu().numpy()
+            if t:
+                outside = np.ones(t, bool)
+                outside[rows] = False
+                raw = o.raw[:o.nbytes].cpu().numpy().reshape(t, -1)
+                assert np.all(raw[outside] == POISON), (k, name, "a row outside the range was written")
+        if rows.stop <= rows.start:
+            continue
+        ins = {kk: v[rows] for kk, v in got.items()}
+        refs = {kk: v[rows] for kk, v in ref.items() if kk in got}
+        if c["quant"] == "mxfp4":
+            from helpers import unpack_fp4
+            compare({kk: ins[kk] for kk in ins if kk in ("residual_out", "norm_out")},
+                    {kk: refs[kk] for kk in refs if kk in ("residual_out", "norm_out")},
+                    "case %d" % k, min_exact=0.0)
+            assert np.array_equal(ins["scale_out"], refs["scale_out"]), k
+            d = np.abs(_ord4(unpack_fp4(ins["quant_out"])) - _ord4(unpack_fp4(refs["quant_out"])))
+            assert d.size == 0 or d.max() <= 1, k
+        else:
+            compare(ins, refs, "case %d" % k, min_exact=0.0)
