@@ -47,8 +47,9 @@ class Args(ctypes.Structure):
 
 def build(force: bool = False) -> str:
     """Compile the oracle into ``oracle/libarf_oracle.so`` and return its path."""
+    header = os.path.join(os.path.dirname(_SRC), "arf_oracle.h")
     if (not force and os.path.exists(_LIB)
-            and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC)):
+            and os.path.getmtime(_LIB) >= max(os.path.getmtime(_SRC), os.path.getmtime(header))):
         return _LIB
     tmp = _LIB + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC",

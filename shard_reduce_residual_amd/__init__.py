@@ -9,7 +9,9 @@ import of a function raises.
 from __future__ import annotations
 
 import ctypes
+import glob
 import os
+import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libarfuse.so")
@@ -69,6 +71,14 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise ImportError("libarfuse.so is not built (%s); run "
                               "`python -m shard_reduce_residual_amd.build`" % LIB_PATH)
+        built = os.path.getmtime(LIB_PATH)
+        newer = [f for f in glob.glob(os.path.join(HERE, "csrc", "*")) +
+                 [os.path.join(os.path.dirname(HERE), "include", "arfuse.h")]
+                 if os.path.exists(f) and os.path.getmtime(f) > built]
+        if newer:
+            sys.stderr.write("warning: libarfuse.so is older than %s; rebuild with "
+                             "`python -m shard_reduce_residual_amd.build`\n"
+                             % ", ".join(os.path.basename(f) for f in newer))
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(L, name)
