@@ -757,6 +757,69 @@ def test_graph_capture_and_replay():
             assert np.array_equal(got[key], eager[key]), (k, key)
 
 
+def test_graph_capture_of_mixed_calls():
+    # several different calls in one captured graph: MXFP4 over a row range with
+    # partial-type accumulation, per-tensor fp8, and the token-slice composition (reduce a
+    # slice, then the epilogue over all rows from the reduced values); every replay,
+    # with the outputs poisoned eagerly in between, equals the same calls run eagerly
+    w = workloads.WORKLOADS["c2"]
+    say("graph capture of mixed calls %s" % w.name)
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    t, h = w.tokens, w.hidden
+    bf = torch.bfloat16
+    scale = torch.tensor([0.02], dtype=torch.float32, device=DEV)
+
+    def outputs():
+        return dict(r1=torch.empty((t, h), dtype=bf, device=DEV),
+                    n1=torch.empty((t, h), dtype=bf, device=DEV),
+                    q1=torch.empty((t, h // 2), dtype=torch.uint8, device=DEV),
+                    s1=torch.empty((t, h // 32), dtype=torch.uint8, device=DEV),
+                    n2=torch.empty((t, h), dtype=bf, device=DEV),
+                    q2=torch.empty((t, h), dtype=torch.uint8, device=DEV),
+                    sums=torch.empty((t, h), dtype=bf, device=DEV),
+                    r3=torch.empty((t, h), dtype=bf, device=DEV),
+                    n3=torch.empty((t, h), dtype=bf, device=DEV))
+
+    def poison(o):
+        for v in o.values():
+            v.view(torch.uint8).fill_(0xFF)
+
+    def calls(o, stream=None):
+        arf.arf_fused_epilogue(pd_, rd, gd, w.eps, residual_out=o["r1"], norm_out=o["n1"],
+                               quant_out=o["q1"], mode=arf.ARF_QUANT_MXFP4, scale_out=o["s1"],
+                               accumulate=arf.ARF_ACC_PARTIAL, row_begin=0, row_count=40,
+                               stream=stream)
+        arf.arf_reduce_add_rmsnorm_quant(pd_, rd, gd, w.eps, o["q2"], arf.ARF_QUANT_PER_TENSOR,
+                                         scale_in=scale, norm_out=o["n2"], stream=stream)
+        arf.arf_reduce_rows(pd_, o["sums"], row_begin=0, row_count=t, stream=stream)
+        arf.arf_reduce_add_rmsnorm(o["sums"].view(1, t, h), rd, gd, w.eps, residual_out=o["r3"],
+                                   norm_out=o["n3"], stream=stream)
+
+    ref = outputs()
+    poison(ref)
+    calls(ref)
+    torch.cuda.synchronize()
+    ref = {k: v.view(torch.uint8).cpu().numpy() for k, v in ref.items()}
+    # the token-slice composition gives the oneshot result (same rounding steps)
+    assert np.array_equal(ref["n3"], ref["n2"])
+    assert np.all(ref["r1"].reshape(t, -1)[40:] == 0xFF)   # rows outside the range
+    o = outputs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up outside the capture
+        calls(o, stream=side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        calls(o)
+    for k in range(4):
+        poison(o)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for key, v in o.items():
+            assert np.array_equal(v.view(torch.uint8).cpu().numpy(), ref[key]), (k, key)
+
 def test_stream_mix_writes_exactly_its_range():
     for rb, wb, units in ((1 << 20, 1 << 18, 0), (3 * 16384 + 48, 0, 0), (0, 5 * 16384 + 16, 3),
                           (64 << 20, 16 << 20, 1024)):
