@@ -270,3 +270,40 @@ def test_binding_rejects_host_tensors_before_any_call():
         arf.arf_e4m3_encode(torch.zeros(8), torch.zeros(8, dtype=torch.uint8))
     with pytest.raises(ValueError, match="device tensor"):
         arf.arf_stream_copy(r, r)
+
+
+def _prototypes():
+    """name -> list of parameter declarations, from include/arfuse.h."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(arf_\w+)\s*\(([^;{]*?)\)\s*;", text):
+        params = [p.strip() for p in m.group(2).split(",") if p.strip()]
+        out[m.group(1)] = [] if params == ["void"] else params
+    return out
+
+
+def test_binding_signatures_follow_the_header():
+    # argument count and pointer-ness of every parameter agree with the C prototypes
+    protos = _prototypes()
+    assert set(protos) == set(arf.SIGNATURES)
+    for name, (res, args) in arf.SIGNATURES.items():
+        params = protos[name]
+        assert len(params) == len(args), name
+        for decl, ct in zip(params, args):
+            is_ptr = "*" in decl
+            assert is_ptr == (ct is ctypes.c_void_p or ct is ctypes.c_char_p or
+                              hasattr(ct, "contents") or ct.__name__.startswith("LP_")), (name, decl)
+
+
+def test_params_struct_follows_the_header():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct arf_params \{(.*?)\} arf_params;", text, flags=re.S).group(1)
+    fields = [l.strip().rstrip(";") for l in body.splitlines() if l.strip()]
+    names = [f.split()[-1].lstrip("*") for f in fields]
+    assert names == [n for n, _ in arf.arf_params._fields_]
+    sizes = {"uint32_t": 4, "int32_t": 4, "int64_t": 8, "float": 4}
+    for f, (n, ct) in zip(fields, arf.arf_params._fields_):
+        if "*" in f:
+            assert ct is ctypes.c_void_p, n
+        else:
+            assert ctypes.sizeof(ct) == sizes[f.split()[0]], n
