@@ -363,3 +363,20 @@ def test_negative_zeros_stay_negative():
     # +0 residual: -0 + +0 = +0
     out = _run(p, np.zeros((2, h), np.uint16), g, 1e-6, "bf16", "bf16")
     assert np.all(out["residual_out"] == 0x0000)
+
+
+def test_oracle_args_struct_follows_its_header():
+    import ctypes
+    import os
+    import re
+    hdr = os.path.join(os.path.dirname(oracle.__file__), "arf_oracle.h")
+    text = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
+    body = re.search(r"typedef struct arfo_args \{(.*?)\} arfo_args;", text, flags=re.S).group(1)
+    fields = [l.strip().rstrip(";") for l in body.splitlines() if l.strip()]
+    assert [f.split()[-1].lstrip("*") for f in fields] == [n for n, _ in oracle.Args._fields_]
+    sizes = {"int32_t": 4, "int64_t": 8, "float": 4}
+    for f, (n, ct) in zip(fields, oracle.Args._fields_):
+        if "*" in f:
+            assert ct is ctypes.c_void_p, n
+        else:
+            assert ctypes.sizeof(ct) == sizes[f.split()[0]], n
