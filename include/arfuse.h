@@ -25,9 +25,11 @@
  *   - Buffers are DEVICE pointers owned by the caller; the library allocates nothing,
  *     keeps no state between calls (apart from a per-device compute-unit count and the
  *     test-only override below) and never synchronises.
- *   - `stream` is a hipStream_t (NULL = the legacy default stream). On ARF_OK exactly one
- *     kernel has been enqueued on it (none when tokens == 0). Kernel faults surface at
- *     the caller's next synchronisation, as usual in HIP.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream). On ARF_OK one kernel
+ *     has been enqueued on it (none when tokens == 0; several, in row order, when a
+ *     one-row-per-workgroup or one-row-per-wavefront grid would exceed the 2^32 - 1
+ *     work-items of one dispatch, which takes tens of millions of rows). Kernel faults
+ *     surface at the caller's next synchronisation, as usual in HIP.
  *   - All arguments are validated before any HIP call: on any error status nothing is
  *     enqueued and nothing is written. Sizes, types and eps are checked first; a call
  *     with tokens == 0 is then complete (ARF_OK) and its pointers are not examined.
@@ -141,7 +143,8 @@ arf_status arf_reduce_add_rmsnorm_quant(const void* partials, int32_t n_shards,
  *                the low nibble, 16-byte aligned); scale_out [tokens][hidden/32] uint8
  *                E8M0 codes, X = 2^(code - 127) = 2^(floor(log2 max|y|) - 2) per block of
  *                32 (code 0 for an all-zero block); codes = E2M1(y / X), round to nearest
- *                even, saturating at +-6.
+ *                even, saturating at +-6. E2M1 has no NaN or infinity: NaN and +-inf give
+ *                +-6 (code 7 with the sign bit); NaN elements do not enter max|y|.
  */
 typedef struct arf_params {
     uint32_t struct_size;
@@ -189,11 +192,14 @@ const char* arf_status_string(int32_t status);
 int32_t arf_version(void);
 
 /*
- * Launch geometry that a call with these sizes would use, without a device call when
- * num_cus > 0 (num_cus <= 0: the current device's compute-unit count is queried, which
- * may return ARF_ERR_HIP). out[0] = path (1 row per wavefront, 2 row per workgroup),
- * out[1] = wavefronts per workgroup, out[2] = 16-byte chunks (8 elements) per lane,
- * out[3] = workgroups in the grid. Honours arf_set_path_override.
+ * Launch geometry that a call with these sizes and no quantised copy would use, without a
+ * device call when num_cus > 0 (then 160 KiB of LDS per workgroup is assumed; num_cus <= 0:
+ * the current device's compute-unit count and LDS size are queried, which may return
+ * ARF_ERR_HIP). out[0] = path: 1 row per wavefront, 2 row per workgroup, 3 held rows (one
+ * workgroup per compute unit reads a batch of rows, keeping each row's rounded residual in
+ * LDS, then writes their outputs); out[1] = wavefronts per workgroup; out[2] = 16-byte
+ * chunks (8 elements) per lane; out[3] = workgroups in the grid (as an unsigned 32-bit
+ * value). Honours arf_set_path_override.
  */
 arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
                         int32_t partial_dtype, int32_t num_cus, int32_t* out);
@@ -201,9 +207,10 @@ arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
 /*
  * TEST AND TUNING ONLY; process-wide, not to be changed while other threads call the
  * library. path 0 = automatic (the other two arguments must be 0); 1 = one row per
- * wavefront; 2 = one row per workgroup. waves_per_block (1 row per workgroup only:
- * 4, 8 or 16) and chunks_per_lane (1, 2, 4 or 8) force the geometry when non-zero.
- * A forced geometry that cannot cover a call's hidden size makes that call return
+ * wavefront; 2 = one row per workgroup; 3 = held rows (4 wavefronts; rows of up to 16384
+ * elements; arf_reduce_rows keeps its automatic plan). waves_per_block (path 2: 4, 8 or
+ * 16; paths 1 and 3: 0 or 4) and chunks_per_lane (1, 2, 4 or 8) force the geometry when
+ * non-zero. A forced geometry that cannot cover a call's hidden size makes that call return
  * ARF_ERR_VALUE. Returns ARF_ERR_VALUE for values outside these sets.
  */
 arf_status arf_set_path_override(int32_t path, int32_t waves_per_block,

@@ -64,6 +64,7 @@ struct Params {
     int32_t quant_mode;
     int32_t acc_partial;       // round every partial sum to the partial type
     int32_t reduce_only;       // store the reduced value and stop
+    int32_t held_rows;         // held-row kernel: rows a workgroup holds at once (K)
 };
 
 struct ActBF16 {};
@@ -144,12 +145,15 @@ __device__ __forceinline__ uint32_t mx_scale_code(float amax) {
 
 // E2M1 code of v: round to nearest even over {0, 0.5, 1, 1.5, 2, 3, 4, 6}, saturating at 6.
 // Each comparison is a decision boundary; a tie goes to the even code (0.25 -> 0,
-// 0.75 -> 1.0, 1.25 -> 1.0, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4). Sign in bit 3.
+// 0.75 -> 1.0, 1.25 -> 1.0, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4). Sign in bit 3. E2M1 has
+// no NaN: a NaN saturates like an infinity, to +-6 with its sign bit (every comparison with
+// it is false, so it is caught separately).
 __device__ __forceinline__ uint32_t e2m1_code(float v) {
     const float a = __builtin_fabsf(v);
     uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
                  (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
                  (uint32_t)(a > 5.0f);
+    c = a != a ? 7u : c;
     return c | ((__builtin_bit_cast(uint32_t, v) >> 28) & 0x8u);
 }
 
@@ -539,6 +543,276 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
     }
 }
 
+// ---- the held-row kernel ----------------------------------------------------------------
+//
+// Persistent workgroups (at most one per compute unit), each owning whole rows. A workgroup
+// works in batches of up to K rows:
+//  * read half: it streams its rows (shards shard-major, then the residual; the first D-1
+//    shards of the next row are loaded while the current row finishes) and keeps each row's
+//    rounded residual r in LDS, plus each wavefront's part of sum(r^2);
+//  * write half: for each held row it stores residual_out, recomputes y = cast((r*inv)*gamma)
+//    from r, inv and gamma, and stores norm_out and the quantised copy.
+// When the whole launch fits in one batch per workgroup, HBM sees one long stretch of reads
+// and then one of writes, instead of reads and writes interleaved row by row (a bus
+// turnaround each time). Workgroup g takes rows g, g + G, g + 2G, ... in batches of K, so at
+// any moment the chip works on one compact window of rows.
+//
+// The arithmetic, and its order, is that of fused_reduce_add_rmsnorm's row-per-workgroup
+// form with the same number of wavefronts: the outputs are the same bits. The write half
+// uses the 16-bit layout for every partial type (lane gl owns 8 consecutive elements per
+// chunk, 16-byte stores): the LDS image of a row is its HBM byte image, and only the lane
+// that computes an element changes; the sum of squares is taken in the read layout and the
+// per-token maximum does not depend on the order.
+//
+// LDS (size set by the host): K rows of hidden*2 bytes, then K*WAVES fp64 partial sums of
+// squares and K*WAVES fp32 maxima. Only hidden/8 <= C * WAVES * 64 is supported (the host
+// checks).
+template <class PT, class AT, int N, int C, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fused_held_rows(Params p) {
+    constexpr int PW = PartTraits<PT>::kPieces;
+    constexpr int G = WAVES * 64;              // lanes per row
+    constexpr int D = N + 1 < 3 ? N + 1 : 3;   // segments in flight (D - 1 <= N)
+    constexpr bool SPLIT = PW == 2;
+    using L = Layout<SPLIT, G>;
+    using LW = Layout<false, G>;
+    extern __shared__ __align__(16) char s_dyn[];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int gl = threadIdx.x;
+    const int K = p.held_rows;
+    const uint32_t H = (uint32_t)p.hidden;
+    const uint32_t act_row = H * 2u;
+    const uint32_t part_row = H * (uint32_t)PartTraits<PT>::kBytes;
+    const uint32_t n_pieces = SPLIT ? H / 4u : H / 8u;   // 8- or 16-byte pieces of a 16-bit row
+    double* s_ss = reinterpret_cast<double*>(s_dyn + (size_t)K * act_row);
+    float* s_mx = reinterpret_cast<float*>(s_ss + K * WAVES);
+
+    const auto g_in = make_rsrc(p.gamma, act_row);
+    u32x4 gv[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j) gv[j] = LW::template load_act<kAuxDefault>(g_in, j, gl);
+    const float scale_tensor = p.quant_mode == kQuantTensor ? p.scale_in[0] : 0.0f;
+
+    auto hold_store = [&](char* row, int j, u32x4 v) {   // chunk j of the read layout
+        if constexpr (SPLIT) {
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+                const uint32_t u = (uint32_t)((2 * j + w) * G + gl);
+                if (u < n_pieces)
+                    *reinterpret_cast<u32x2*>(row + u * 8u) = w ? u32x2{v[2], v[3]} : u32x2{v[0], v[1]};
+            }
+        } else {
+            const uint32_t c = (uint32_t)(j * G + gl);
+            if (c < n_pieces) *reinterpret_cast<u32x4*>(row + c * 16u) = v;
+        }
+    };
+    auto hold_load = [&](const char* row, int j) {   // chunk j of the 16-bit layout
+        u32x4 v = {0u, 0u, 0u, 0u};
+        const uint32_t c = (uint32_t)(j * G + gl);
+        if (c < H / 8u) v = *reinterpret_cast<const u32x4*>(row + c * 16u);
+        return v;
+    };
+    auto shard_rsrc = [&](int64_t row, int r, bool valid) {
+        return make_rsrc((const char*)p.partials + ((int64_t)r * p.tokens + row) * (int64_t)part_row,
+                         valid ? part_row : 0u);
+    };
+    auto row_inv = [&](int k) {
+        double ss = 0.0;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) ss += s_ss[k * WAVES + w];
+        return (float)(1.0 / __builtin_sqrt(ss / (double)H + (double)p.eps));
+    };
+
+    // Workgroup g's i-th row is row_begin + T(i), T(i) = (i / K)*G*K + (i % K)*G + g; rows
+    // of a batch are consecutive i. T(i) >= rows: no more rows (T grows with i).
+    const int64_t rows = p.row_end - p.row_begin;
+    const int64_t grid = gridDim.x;
+    auto ticket = [&](int64_t i) { return (i / K) * (grid * K) + (i % K) * grid + blockIdx.x; };
+    int64_t seq = 0;               // rows taken so far: the current row is T(seq)
+    int64_t cur = ticket(0), nxt = ticket(1);
+
+    u32x4 pf[D - 1][C][PW];   // the first D-1 shards of the next row
+    while (cur < rows) {
+        // ---- read half: up to K rows in, r held in LDS
+        {
+            const auto row0 = p.row_begin + cur;
+#pragma unroll
+            for (int d = 0; d < D - 1; ++d) {
+                const auto rs = shard_rsrc(row0, d, true);
+#pragma unroll
+                for (int j = 0; j < C; ++j)
+#pragma unroll
+                    for (int w = 0; w < PW; ++w)
+                        pf[d][j][w] = __builtin_amdgcn_raw_buffer_load_b128(rs, L::part(j, w, gl), 0, kAuxStream);
+            }
+        }
+        int kn = 0;
+        for (;;) {
+            const int k = kn;
+            const int64_t row = p.row_begin + cur;
+            const bool nvalid = k + 1 < K && nxt < rows;   // the next row joins this batch
+            const int64_t nrow = p.row_begin + (nxt < rows ? nxt : cur);
+            __amdgpu_buffer_rsrc_t part[N];
+#pragma unroll
+            for (int r = 0; r < N; ++r) part[r] = shard_rsrc(row, r, true);
+            const auto r_in = make_rsrc((const char*)p.residual_in + row * (int64_t)act_row, act_row);
+            u32x4 sb[N][C][PW];
+            u32x4 rv[C];
+#pragma unroll
+            for (int d = 0; d < D - 1; ++d)
+#pragma unroll
+                for (int j = 0; j < C; ++j)
+#pragma unroll
+                    for (int w = 0; w < PW; ++w) sb[d][j][w] = pf[d][j][w];
+            float acc[C][8];
+            double ss = 0.0;
+            char* hrow = s_dyn + (size_t)k * act_row;
+#pragma unroll
+            for (int s = 0; s <= N; ++s) {
+                const int t = s + D - 1;   // segment issued now: shard t, the residual (t == N),
+                if (t < N) {               // or shard t - N - 1 of the next row
+#pragma unroll
+                    for (int j = 0; j < C; ++j)
+#pragma unroll
+                        for (int w = 0; w < PW; ++w)
+                            sb[t][j][w] = __builtin_amdgcn_raw_buffer_load_b128(part[t], L::part(j, w, gl), 0, kAuxStream);
+                } else if (t == N) {
+#pragma unroll
+                    for (int j = 0; j < C; ++j) rv[j] = L::template load_act<kAuxStream>(r_in, j, gl);
+                } else {
+                    const auto rs = shard_rsrc(nrow, t - N - 1, nvalid);
+#pragma unroll
+                    for (int j = 0; j < C; ++j)
+#pragma unroll
+                        for (int w = 0; w < PW; ++w)
+                            pf[t - N - 1][j][w] = __builtin_amdgcn_raw_buffer_load_b128(rs, L::part(j, w, gl), 0, kAuxStream);
+                }
+                if (s < N) {
+#pragma unroll
+                    for (int j = 0; j < C; ++j) {
+                        float f[8];
+                        load_partial_chunk(AT{}, sb[s][j], f);
+                        if (s == 0) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) acc[j][e] = f[e];
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) acc[j][e] = acc[j][e] + f[e];
+                            if constexpr (PW == 1) {
+                                float rnd[8];
+                                unpack8(PT{}, pack8(PT{}, acc[j]), rnd);
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) acc[j][e] = p.acc_partial ? rnd[e] : acc[j][e];
+                            }
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < C; ++j) {
+                        float sv[8], res[8], sum[8];
+                        unpack8(AT{}, pack8(AT{}, acc[j]), sv);
+                        unpack8(AT{}, rv[j], res);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) sum[e] = sv[e] + res[e];
+                        const u32x4 rr = pack8(AT{}, sum);
+                        hold_store(hrow, j, rr);
+                        float x[8];
+                        unpack8(AT{}, rr, x);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) ss = __builtin_fma((double)x[e], (double)x[e], ss);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);   // keep the ring: D-1 segments in flight
+            }
+            ss = wave_sum(ss);
+            if (lane == 0) s_ss[k * WAVES + wave] = ss;
+            kn = k + 1;
+            cur = nxt;
+            nxt = ticket(++seq + 1);
+            if (!nvalid) break;
+        }
+        __syncthreads();
+
+        // ---- per-token maxima of the cast outputs (needed before the first code is written)
+        if (p.quant_mode == kQuantToken) {
+            for (int k = 0; k < kn; ++k) {
+                const float inv = row_inv(k);
+                const char* hrow = s_dyn + (size_t)k * act_row;
+                float amax = 0.0f;
+#pragma unroll
+                for (int j = 0; j < C; ++j) {
+                    float x[8], g[8], y[8], yc[8];
+                    unpack8(AT{}, hold_load(hrow, j), x);
+                    unpack8(AT{}, gv[j], g);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        float v = x[e] * inv;
+                        y[e] = v * g[e];
+                    }
+                    unpack8(AT{}, pack8(AT{}, y), yc);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, __builtin_fabsf(yc[e]));
+                }
+                amax = wave_max(amax);
+                if (lane == 0) s_mx[k * WAVES + wave] = amax;
+            }
+            __syncthreads();
+        }
+
+        // ---- write half (the batch's rows are T(seq - kn) .. T(seq - 1))
+        for (int k = 0; k < kn; ++k) {
+            const int64_t row = p.row_begin + ticket(seq - kn + k);
+            const int64_t act_off = row * (int64_t)act_row;
+            const auto r_out = make_rsrc((char*)p.residual_out + act_off, p.residual_out ? act_row : 0u);
+            const auto y_out = make_rsrc((char*)p.norm_out + act_off, p.norm_out ? act_row : 0u);
+            const char* hrow = s_dyn + (size_t)k * act_row;
+            const float inv = row_inv(k);
+            float inv_scale = 0.0f;
+            if (p.quant_mode == kQuantToken) {
+                float amax = 0.0f;
+#pragma unroll
+                for (int w = 0; w < WAVES; ++w) amax = fmaxf(amax, s_mx[k * WAVES + w]);
+                const float scale = amax / 448.0f;
+                if (gl == 0) static_cast<float*>(p.scale_out)[row] = scale;
+                inv_scale = scale > 0.0f ? 1.0f / scale : 0.0f;
+            } else if (p.quant_mode == kQuantTensor) {
+                inv_scale = scale_tensor > 0.0f ? 1.0f / scale_tensor : 0.0f;
+            }
+            const auto q_out = make_rsrc(p.quant_out + row * (int64_t)H, p.quant_out ? H : 0u);
+            const auto q_mx = make_rsrc(p.quant_out + row * (int64_t)(H / 2), p.quant_out ? H / 2 : 0u);
+            const auto s_mxo = make_rsrc((uint8_t*)p.scale_out + row * (int64_t)(H / 32), p.scale_out ? H / 32 : 0u);
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                const u32x4 rr = hold_load(hrow, j);
+                LW::store_act(rr, r_out, j, gl);
+                float x[8], g[8], y[8];
+                unpack8(AT{}, rr, x);
+                unpack8(AT{}, gv[j], g);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float v = x[e] * inv;
+                    y[e] = v * g[e];
+                }
+                const u32x4 yr = pack8(AT{}, y);
+                LW::store_act(yr, y_out, j, gl);
+                if (p.quant_mode == kQuantNone) continue;
+                float yc[8];
+                unpack8(AT{}, yr, yc);
+                if (p.quant_mode == kQuantMx) {
+                    LW::store_mx(yc, q_mx, s_mxo, j, gl);
+                } else {
+                    u32x2 q;
+                    q[0] = e4m3x4(yc[0] * inv_scale, yc[1] * inv_scale, yc[2] * inv_scale, yc[3] * inv_scale);
+                    q[1] = e4m3x4(yc[4] * inv_scale, yc[5] * inv_scale, yc[6] * inv_scale, yc[7] * inv_scale);
+                    LW::store_codes(q, q_out, j, gl);
+                }
+            }
+        }
+        __syncthreads();   // the next batch reuses the LDS rows
+    }
+}
+
 // Host-side launcher for one instantiation; returns the launch's own status.
 template <class PT, class AT, int N, int C, int WAVES, bool ROW_PER_WAVE, int DEPTH = 2>
 hipError_t launch_fused(const Params& p, uint32_t grid, hipStream_t stream) {
@@ -551,5 +825,17 @@ hipError_t launch_fused(const Params& p, uint32_t grid, hipStream_t stream) {
 }
 
 typedef hipError_t (*launch_fn)(const Params&, uint32_t, hipStream_t);
+
+// Held-row kernel launcher: `lds` bytes of dynamic LDS per workgroup.
+template <class PT, class AT, int N, int C, int WAVES>
+hipError_t launch_held(const Params& p, uint32_t grid, uint32_t lds, hipStream_t stream) {
+    Params arg = p;
+    void* args[] = {&arg};
+    return hipLaunchKernel(
+        reinterpret_cast<const void*>(&fused_held_rows<PT, AT, N, C, WAVES>),
+        dim3(grid), dim3(WAVES * 64), args, lds, stream);
+}
+
+typedef hipError_t (*held_launch_fn)(const Params&, uint32_t, uint32_t, hipStream_t);
 
 }  // namespace arf

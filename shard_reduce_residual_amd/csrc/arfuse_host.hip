@@ -5,6 +5,7 @@
 // Every argument is validated before the first HIP call. The only device queries are
 // hipGetDevice and the compute-unit count (cached per device).
 #include <atomic>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 
@@ -13,18 +14,8 @@
 
 namespace {
 
+using arf::held_launch_fn;
 using arf::launch_fn;
-
-constexpr int kMaxDevices = 64;
-std::atomic<int> g_cu_count[kMaxDevices];   // 0 = not queried yet
-std::atomic<int> g_path{0}, g_waves{0}, g_chunks{0};
-
-struct Plan {
-    int path;      // 1 row per wavefront, 2 row per workgroup
-    int waves;     // wavefronts per workgroup
-    int chunks;    // 16-byte chunks per lane
-    uint32_t grid; // workgroups
-};
 
 bool in_menu_c(int c) { return c == 1 || c == 2 || c == 4 || c == 8; }
 bool in_menu_w(int w) { return w == 4 || w == 8 || w == 16; }
@@ -35,6 +26,55 @@ int pow2_at_least(int64_t v) {
     return p;
 }
 int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];   // 0 = not queried yet
+std::atomic<int> g_lds_bytes[kMaxDevices];  // LDS bytes a workgroup may use; 0 = not queried
+std::atomic<int> g_path{0}, g_waves{0}, g_chunks{0};
+
+struct Plan {
+    int path;      // 1 row per wavefront, 2 row per workgroup, 3 held rows
+    int waves;     // wavefronts per workgroup
+    int chunks;    // 16-byte chunks per lane
+    uint32_t grid; // workgroups
+    int held;      // held-row kernel: rows per workgroup and phase
+    uint32_t lds;  // held-row kernel: dynamic LDS bytes per workgroup
+};
+
+struct DeviceInfo {
+    int cus;       // compute units
+    int lds;       // LDS bytes one workgroup may allocate
+};
+
+// Held-row kernel geometry: 4 wavefronts, one workgroup per compute unit, each holding up to
+// as many rows as its LDS takes (the row's residual plus 12 bytes per wavefront for the
+// partial sums of squares and the per-token maxima). Rows are spread evenly over the
+// phases. Returns false when the row does not fit the kernel's menu (more than 8 chunks per
+// lane, or a single row larger than the LDS).
+constexpr int kHeldWaves = 4;
+// LDS per workgroup assumed by arf_get_plan when the caller gives a CU count instead of
+// querying a device: gfx950's 160 KiB.
+constexpr int kPlanLdsBytes = 160 * 1024;
+bool held_plan(int64_t rows, int32_t hidden, const DeviceInfo& dev, int chunks, Plan* pl) {
+    const int hc = hidden / 8;
+    if (chunks == 0) chunks = pow2_at_least(div_up(hc, kHeldWaves * 64));
+    if (chunks > 8 || kHeldWaves * 64 * chunks < hc) return false;
+    // per held row: the residual plus each wavefront's sum of squares and maximum
+    const int64_t per_row = (int64_t)hidden * 2 + kHeldWaves * 12;
+    const int64_t kmax = dev.lds / per_row;
+    if (kmax < 1) return false;
+    const int64_t grid = rows < dev.cus ? rows : dev.cus;
+    const int64_t phases = div_up(rows, grid * kmax);
+    const int64_t k = div_up(rows, grid * phases);
+    pl->path = 3;
+    pl->waves = kHeldWaves;
+    pl->chunks = chunks;
+    pl->grid = (uint32_t)grid;
+    pl->held = (int)k;
+    pl->lds = (uint32_t)(k * per_row);
+    return true;
+}
+
 
 // Launch geometry: the hidden/8 chunks of a row are spread over the lanes that own it.
 // Fitted to sweeps on MI355X (256 CUs) over hidden 1024..16384, 128..8192 tokens, 2 and 8
@@ -50,9 +90,37 @@ int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //    - otherwise 4 wavefronts with up to 8 chunks per lane, so that several rows share a
 //      compute unit;
 //    - rows too wide for 8 chunks per lane use 16 wavefronts.
-arf_status make_plan(int64_t tokens, int32_t hidden, int num_cus, Plan* pl) {
+//  * held rows (path 3) where that measured faster (sweep of 175 shapes, bit-identical
+//    outputs): at most 4 shards, 4096 <= hidden <= 8192, no quantised copy, 6 to 16 rows
+//    per compute unit and no more than one batch per workgroup holds. There HBM sees the whole
+//    launch's reads, then its writes: 2-10% faster (3% for 4 fp32 shards of 2048 x 7168). With more shards, other
+//    row sizes, several batches, or the per-token scale's extra pass over the held rows, it
+//    was slower than one row per workgroup.
+bool held_wins(int64_t tokens, int32_t hidden, int n, int quant, const DeviceInfo& dev,
+               Plan* pl) {
+    if (n > 4 || hidden < 4096 || hidden > 8192 || quant != arf::kQuantNone ||
+        tokens < 6LL * dev.cus || tokens > 16LL * dev.cus)
+        return false;
+    Plan h;
+    if (!held_plan(tokens, hidden, dev, 0, &h)) return false;
+    if ((int64_t)h.grid * h.held < tokens) return false;   // more than one batch
+    *pl = h;
+    return true;
+}
+
+arf_status make_plan(int64_t tokens, int32_t hidden, int n, int quant, const DeviceInfo& dev,
+                     bool reduce_only, Plan* pl) {
     const int hc = hidden / 8;
+    const int num_cus = dev.cus;
     int path = g_path.load(), waves = g_waves.load(), chunks = g_chunks.load();
+    pl->held = 0;
+    pl->lds = 0;
+    if (path == 3) {
+        // the held-row kernel has no reduce-only form: such calls take the default plan
+        if (!reduce_only) return held_plan(tokens, hidden, dev, chunks, pl) ? ARF_OK : ARF_ERR_VALUE;
+        path = waves = chunks = 0;
+    }
+    if (path == 0 && !reduce_only && held_wins(tokens, hidden, n, quant, dev, pl)) return ARF_OK;
     if (path == 0) {
         waves = chunks = 0;
         const bool many_rows = tokens >= 2LL * num_cus;
@@ -88,6 +156,21 @@ arf_status make_plan(int64_t tokens, int32_t hidden, int num_cus, Plan* pl) {
     return ARF_OK;
 }
 
+held_launch_fn lookup_held(int pdt, int adt, int n, int c) {
+#define ARF_BY_RANGE(PD, AD)                                          \
+    if (n <= 4) return arf::held_##PD##_##AD##_n01_04(n, c);          \
+    if (n <= 8) return arf::held_##PD##_##AD##_n05_08(n, c);          \
+    if (n <= 12) return arf::held_##PD##_##AD##_n09_12(n, c);         \
+    return arf::held_##PD##_##AD##_n13_16(n, c);
+    if (adt == ARF_BF16) {
+        if (pdt == ARF_F32) { ARF_BY_RANGE(f32, bf16) }
+        ARF_BY_RANGE(bf16, bf16)
+    }
+    if (pdt == ARF_F32) { ARF_BY_RANGE(f32, f16) }
+    ARF_BY_RANGE(f16, f16)
+#undef ARF_BY_RANGE
+}
+
 launch_fn lookup(int pdt, int adt, int n, const Plan& pl) {
     const bool rpw = pl.path == 1;
     const int w = pl.waves, c = pl.chunks;
@@ -105,20 +188,37 @@ launch_fn lookup(int pdt, int adt, int n, const Plan& pl) {
 #undef ARF_BY_RANGE
 }
 
-arf_status device_cus(int* cus) {
+arf_status device_info(DeviceInfo* info) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ARF_ERR_HIP;
     if (dev < kMaxDevices) {
-        int c = g_cu_count[dev].load(std::memory_order_relaxed);
-        if (c > 0) { *cus = c; return ARF_OK; }
+        const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+        const int l = g_lds_bytes[dev].load(std::memory_order_relaxed);
+        if (c > 0 && l > 0) {
+            *info = DeviceInfo{c, l};
+            return ARF_OK;
+        }
     }
-    int c = 0;
+    int c = 0, l = 0;
     if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         c <= 0)
         return ARF_ERR_HIP;
-    if (dev < kMaxDevices) g_cu_count[dev].store(c, std::memory_order_relaxed);
-    *cus = c;
+    if (hipDeviceGetAttribute(&l, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+        l <= 0)
+        return ARF_ERR_HIP;
+    if (dev < kMaxDevices) {
+        g_cu_count[dev].store(c, std::memory_order_relaxed);
+        g_lds_bytes[dev].store(l, std::memory_order_relaxed);
+    }
+    *info = DeviceInfo{c, l};
     return ARF_OK;
+}
+
+arf_status device_cus(int* cus) {
+    DeviceInfo info;
+    const arf_status st = device_info(&info);
+    if (st == ARF_OK) *cus = info.cus;
+    return st;
 }
 
 struct Range {
@@ -218,12 +318,16 @@ arf_status validate(Call& c) {
 arf_status run(Call c, void* stream) {
     arf_status st = validate(c);
     if (st != ARF_OK || c.row_count == 0) return st;
-    int cus = 0;
-    if ((st = device_cus(&cus)) != ARF_OK) return st;
+    DeviceInfo dev;
+    if ((st = device_info(&dev)) != ARF_OK) return st;
     Plan pl;
-    if ((st = make_plan(c.row_count, c.hidden, cus, &pl)) != ARF_OK) return st;
-    launch_fn fn = lookup(c.pdt, c.adt, c.n, pl);
-    if (!fn) return ARF_ERR_VALUE;
+    if ((st = make_plan(c.row_count, c.hidden, c.n, c.quant, dev, c.reduce_only, &pl)) != ARF_OK)
+        return st;
+    launch_fn fn = nullptr;
+    held_launch_fn hfn = nullptr;
+    if (pl.path == 3) hfn = lookup_held(c.pdt, c.adt, c.n, pl.chunks);
+    else fn = lookup(c.pdt, c.adt, c.n, pl);
+    if (!fn && !hfn) return ARF_ERR_VALUE;
     arf::Params p;
     p.partials = c.partials;
     p.residual_in = c.reduce_only ? nullptr : c.residual_in;
@@ -242,7 +346,21 @@ arf_status run(Call c, void* stream) {
     p.quant_mode = c.reduce_only ? arf::kQuantNone : c.quant;
     p.acc_partial = c.acc == ARF_ACC_PARTIAL;
     p.reduce_only = c.reduce_only;
-    if (fn(p, pl.grid, (hipStream_t)stream) != hipSuccess) return ARF_ERR_HIP;
+    p.held_rows = pl.held;
+    if (hfn)   // at most one workgroup per compute unit, looping over its rows
+        return hfn(p, pl.grid, pl.lds, (hipStream_t)stream) == hipSuccess ? ARF_OK : ARF_ERR_HIP;
+    // One dispatch covers at most 2^32 - 1 work-items: a grid that would exceed that is
+    // split into consecutive row ranges, one kernel each, enqueued in row order.
+    const int64_t threads = pl.path == 1 ? 256 : 64LL * pl.waves;
+    const int64_t rows_per_wg = pl.path == 1 ? 4 : 1;
+    const int64_t max_rows = ((int64_t)UINT32_MAX / threads) * rows_per_wg;
+    const int64_t end = c.row_begin + c.row_count;
+    for (int64_t b = c.row_begin; b < end; b += max_rows) {
+        p.row_begin = b;
+        p.row_end = end - b < max_rows ? end : b + max_rows;
+        const uint32_t grid = (uint32_t)((p.row_end - b + rows_per_wg - 1) / rows_per_wg);
+        if (fn(p, grid, (hipStream_t)stream) != hipSuccess) return ARF_ERR_HIP;
+    }
     return ARF_OK;
 }
 
@@ -416,12 +534,13 @@ arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
         return ARF_ERR_SHAPE;
     if (partial_dtype != ARF_BF16 && partial_dtype != ARF_F16 && partial_dtype != ARF_F32)
         return ARF_ERR_DTYPE;
+    DeviceInfo dev{num_cus, kPlanLdsBytes};
     if (num_cus <= 0) {
-        arf_status st = device_cus(&num_cus);
+        arf_status st = device_info(&dev);
         if (st != ARF_OK) return st;
     }
     Plan pl;
-    arf_status st = make_plan(tokens, hidden, num_cus, &pl);
+    arf_status st = make_plan(tokens, hidden, n_shards, arf::kQuantNone, dev, false, &pl);
     if (st != ARF_OK) return st;
     out[0] = pl.path;
     out[1] = pl.waves;
@@ -432,13 +551,13 @@ arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
 
 arf_status arf_set_path_override(int32_t path, int32_t waves_per_block,
                                  int32_t chunks_per_lane) {
-    if (path < 0 || path > 2) return ARF_ERR_VALUE;
+    if (path < 0 || path > 3) return ARF_ERR_VALUE;
     if (path == 0 && (waves_per_block || chunks_per_lane)) return ARF_ERR_VALUE;
-    if (path == 1 && waves_per_block && waves_per_block != 4) return ARF_ERR_VALUE;
+    if ((path == 1 || path == 3) && waves_per_block && waves_per_block != 4) return ARF_ERR_VALUE;
     if (path == 2 && waves_per_block && !in_menu_w(waves_per_block)) return ARF_ERR_VALUE;
     if (chunks_per_lane && !in_menu_c(chunks_per_lane)) return ARF_ERR_VALUE;
     g_path.store(path);
-    g_waves.store(path == 2 ? waves_per_block : 0);
+    g_waves.store(path == 2 ? waves_per_block : 0);   // paths 1 and 3 always use 4
     g_chunks.store(chunks_per_lane);
     return ARF_OK;
 }

@@ -1,6 +1,6 @@
-// arfuse_table.hpp -- the instantiated launch geometries of the fused kernel, and the
-// lookup from (shard count, path, wavefronts per workgroup, chunks per lane) to a
-// launcher. Each inst_*.hip translation unit instantiates one element-type pair for a
+// arfuse_table.hpp -- the instantiated launch geometries of the fused kernel and of the
+// held-row kernel, and the lookup from (shard count, path, wavefronts per workgroup,
+// chunks per lane) to a launcher. Each inst_*.hip translation unit instantiates one element-type pair for a
 // range of shard counts, so the 1024 kernels compile in parallel.
 //
 // Menu: shard count N in 1..16 (exact: no per-shard branch, so the loads of a whole row
@@ -64,12 +64,39 @@ launch_fn pick_shards(int n, bool row_per_wave, int waves, int c) {
     }
 }
 
+// Held-row kernel: 4 wavefronts (one per SIMD, so each may use the whole register file),
+// chunks per lane in {1, 2, 4, 8}: rows of up to 16384 elements.
+template <class PT, class AT, int N>
+held_launch_fn pick_held(int c) {
+    switch (c) {
+        case 1: return &launch_held<PT, AT, N, 1, 4>;
+        case 2: return &launch_held<PT, AT, N, 2, 4>;
+        case 4: return &launch_held<PT, AT, N, 4, 4>;
+        case 8: return &launch_held<PT, AT, N, 8, 4>;
+        default: return nullptr;
+    }
+}
+
+template <class PT, class AT, int NLO, int NHI>
+held_launch_fn pick_held_shards(int n, int c) {
+    if constexpr (NLO <= NHI) {
+        if (n == NLO) return pick_held<PT, AT, NLO>(c);
+        return pick_held_shards<PT, AT, NLO + 1, NHI>(n, c);
+    } else {
+        return nullptr;
+    }
+}
+
 // Defined in the inst_<partial>_<activation>_n<lo>_<hi>.hip translation units.
 #define ARF_DECLARE_LOOKUPS(PD, AD)                                              \
     launch_fn lookup_##PD##_##AD##_n01_04(int n, bool rpw, int waves, int c);    \
     launch_fn lookup_##PD##_##AD##_n05_08(int n, bool rpw, int waves, int c);    \
     launch_fn lookup_##PD##_##AD##_n09_12(int n, bool rpw, int waves, int c);    \
-    launch_fn lookup_##PD##_##AD##_n13_16(int n, bool rpw, int waves, int c);
+    launch_fn lookup_##PD##_##AD##_n13_16(int n, bool rpw, int waves, int c);    \
+    held_launch_fn held_##PD##_##AD##_n01_04(int n, int c);                      \
+    held_launch_fn held_##PD##_##AD##_n05_08(int n, int c);                      \
+    held_launch_fn held_##PD##_##AD##_n09_12(int n, int c);                      \
+    held_launch_fn held_##PD##_##AD##_n13_16(int n, int c);
 ARF_DECLARE_LOOKUPS(bf16, bf16)
 ARF_DECLARE_LOOKUPS(f16, f16)
 ARF_DECLARE_LOOKUPS(f32, bf16)

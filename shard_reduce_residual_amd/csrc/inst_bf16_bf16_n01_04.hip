@@ -1,8 +1,11 @@
-// Instantiations of the fused kernel for partials ActBF16, activations ActBF16, N = 1..4.
+// Instantiations of the fused and held-row kernels for partials ActBF16, activations ActBF16, N = 1..4.
 #include "arfuse_table.hpp"
 
 namespace arf {
 launch_fn lookup_bf16_bf16_n01_04(int n, bool rpw, int waves, int c) {
     return pick_shards<ActBF16, ActBF16, 1, 4>(n, rpw, waves, c);
+}
+held_launch_fn held_bf16_bf16_n01_04(int n, int c) {
+    return pick_held_shards<ActBF16, ActBF16, 1, 4>(n, c);
 }
 }  // namespace arf

@@ -11,8 +11,9 @@
 #include "arfuse_table.hpp"
 
 namespace arf {
-#define ARF_STUB(PD, AD, R) \
-    launch_fn lookup_##PD##_##AD##_##R(int, bool, int, int) { return nullptr; }
+#define ARF_STUB(PD, AD, R)                                                         \
+    launch_fn lookup_##PD##_##AD##_##R(int, bool, int, int) { return nullptr; }     \
+    held_launch_fn held_##PD##_##AD##_##R(int, int) { return nullptr; }
 #define ARF_STUBS(PD, AD) \
     ARF_STUB(PD, AD, n01_04) ARF_STUB(PD, AD, n05_08) ARF_STUB(PD, AD, n09_12) ARF_STUB(PD, AD, n13_16)
 ARF_STUBS(bf16, bf16)
@@ -22,6 +23,7 @@ ARF_STUBS(f32, f16)
 }  // namespace arf
 
 static int g_checks = 0, g_fail = 0;
+static int64_t div_up_i64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 #define EXPECT(cond)                                                        \
     do {                                                                    \
         ++g_checks;                                                         \
@@ -124,14 +126,23 @@ int main() {
     for (int cus : cus_list)
         for (int64_t t : tok_list)
             for (int h = 8; h <= ARF_MAX_HIDDEN; h += (h < 1024 ? 8 : (h < 8192 ? 136 : 2056))) {
-                int32_t o[4];
-                if (arf_get_plan(3, t, h, ARF_BF16, cus, o) != ARF_OK) { EXPECT(false); continue; }
-                const int64_t lanes = o[0] == 1 ? 64 : 64 * (int64_t)o[1];
-                EXPECT(o[0] == 1 || o[0] == 2);
-                EXPECT(o[2] == 1 || o[2] == 2 || o[2] == 4 || o[2] == 8);
-                EXPECT(o[0] == 1 ? o[1] == 4 : (o[1] == 4 || o[1] == 8 || o[1] == 16));
-                EXPECT(lanes * o[2] * 8 >= h);
-                EXPECT((int64_t)(uint32_t)o[3] == (o[0] == 1 ? (t + 3) / 4 : t));
+                for (int n : {3, 8}) {
+                    int32_t o[4];
+                    if (arf_get_plan(n, t, h, ARF_BF16, cus, o) != ARF_OK) { EXPECT(false); continue; }
+                    const int64_t lanes = o[0] == 1 ? 64 : 64 * (int64_t)o[1];
+                    EXPECT(o[0] == 1 || o[0] == 2 || (o[0] == 3 && n <= 4));
+                    EXPECT(o[2] == 1 || o[2] == 2 || o[2] == 4 || o[2] == 8);
+                    EXPECT(o[0] == 2 ? (o[1] == 4 || o[1] == 8 || o[1] == 16) : o[1] == 4);
+                    EXPECT(lanes * o[2] * 8 >= h);
+                    // held rows: one workgroup per compute unit, the whole launch in one batch
+                    // of at most 160 KiB of LDS per workgroup
+                    const int64_t g = o[0] == 1 ? (t + 3) / 4 : (o[0] == 2 ? t : (t < cus ? t : cus));
+                    EXPECT((int64_t)(uint32_t)o[3] == g);
+                    if (o[0] == 3) {
+                        EXPECT(t >= 6LL * cus && t <= 16LL * cus && h >= 4096 && h <= 8192);
+                        EXPECT(div_up_i64(t, cus) * (2LL * h + 48) <= 160 * 1024);
+                    }
+                }
             }
     int32_t o[4];
     EXPECT(arf_get_plan(3, 8, 64, ARF_BF16, 256, nullptr) == ARF_ERR_NULL);
@@ -146,10 +157,28 @@ int main() {
     EXPECT(arf_get_plan(3, 100, 65536, ARF_BF16, 256, o) == ARF_OK && o[1] == 16 && o[2] == 8);
     EXPECT(arf_set_path_override(2, 4, 1) == ARF_OK);
     EXPECT(arf_get_plan(3, 100, 4096, ARF_BF16, 256, o) == ARF_ERR_VALUE);
-    const int bad[][3] = {{3, 0, 0}, {-1, 0, 0}, {0, 4, 0}, {0, 0, 2}, {1, 8, 0}, {2, 3, 0}, {2, 4, 3}, {2, 32, 1}};
+    // held rows forced: 4 wavefronts, grid min(rows, CUs); refused where a row needs more
+    // than 8 chunks per lane
+    EXPECT(arf_set_path_override(3, 0, 0) == ARF_OK);
+    EXPECT(arf_get_plan(8, 100, 16384, ARF_BF16, 256, o) == ARF_OK && o[0] == 3 && o[1] == 4 && o[2] == 8 && o[3] == 100);
+    EXPECT(arf_get_plan(8, 8192, 1024, ARF_BF16, 256, o) == ARF_OK && o[0] == 3 && o[2] == 1 && o[3] == 256);
+    EXPECT(arf_get_plan(8, 100, 16392, ARF_BF16, 256, o) == ARF_ERR_VALUE);
+    EXPECT(arf_set_path_override(3, 4, 2) == ARF_OK);
+    EXPECT(arf_get_plan(8, 100, 4096, ARF_BF16, 256, o) == ARF_OK && o[0] == 3 && o[2] == 2);
+    EXPECT(arf_get_plan(8, 100, 4104, ARF_BF16, 256, o) == ARF_ERR_VALUE);
+    const int bad[][3] = {{4, 0, 0}, {-1, 0, 0}, {0, 4, 0}, {0, 0, 2}, {1, 8, 0}, {2, 3, 0}, {2, 4, 3}, {2, 32, 1}, {3, 8, 0}, {3, 0, 3}};
     for (const auto& v : bad) EXPECT(arf_set_path_override(v[0], v[1], v[2]) == ARF_ERR_VALUE);
     EXPECT(arf_set_path_override(0, 0, 0) == ARF_OK);
     EXPECT(arf_get_plan(8, 8192, 16384, ARF_BF16, 256, o) == ARF_OK && o[0] == 2 && o[1] == 4 && o[2] == 8);
+    // held rows by default only in their measured range
+    EXPECT(arf_get_plan(4, 2048, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 3 && o[2] == 4 && o[3] == 256);
+    EXPECT(arf_get_plan(8, 2048, 7168, ARF_BF16, 256, o) == ARF_OK && o[0] == 2);
+    EXPECT(arf_get_plan(4, 1535, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 2);
+    EXPECT(arf_get_plan(4, 1536, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 3);
+    EXPECT(arf_get_plan(4, 4096, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 2);   // two batches
+    EXPECT(arf_get_plan(2, 4096, 4096, ARF_BF16, 256, o) == ARF_OK && o[0] == 3);
+    EXPECT(arf_get_plan(2, 4096, 4088, ARF_BF16, 256, o) == ARF_OK && o[0] != 3);
+    EXPECT(arf_get_plan(2, 4097, 4096, ARF_BF16, 256, o) == ARF_OK && o[0] != 3);
 
     std::printf("%s %d checks, %d failed%s\n", g_fail ? "FAILED" : "ok", g_checks, g_fail,
                 have_device ? " (device present: launching calls skipped)" : "");

@@ -119,14 +119,18 @@ def test_plan_covers_the_row_and_follows_the_menu():
     try:
         for h in (8, 64, 264, 1024, 2048, 4096, 7168, 8192, 16384, 32768, 65536):
             for t in (1, 16, 128, 2048, 8192):
-                p = plan(8, t, h)
-                lanes = 64 if p["path"] == 1 else 64 * p["waves"]
-                assert lanes * p["chunks"] * 8 >= h
-                assert p["chunks"] in (1, 2, 4, 8)
-                if p["path"] == 1:
-                    assert p["waves"] == 4 and p["grid"] == (t + 3) // 4
-                else:
-                    assert p["waves"] in (4, 8, 16) and p["grid"] == t
+                for n in (2, 8):
+                    p = plan(n, t, h)
+                    lanes = 64 if p["path"] == 1 else 64 * p["waves"]
+                    assert lanes * p["chunks"] * 8 >= h
+                    assert p["chunks"] in (1, 2, 4, 8)
+                    if p["path"] == 1:
+                        assert p["waves"] == 4 and p["grid"] == (t + 3) // 4
+                    elif p["path"] == 2:
+                        assert p["waves"] in (4, 8, 16) and p["grid"] == t
+                    else:   # held rows: one workgroup per CU, one batch of rows each
+                        assert p["path"] == 3 and n <= 4 and p["waves"] == 4
+                        assert p["grid"] == min(t, 256) and 6 * 256 <= t <= 16 * 256
     finally:
         arf.arf_set_path_override(0)
 
@@ -134,7 +138,7 @@ def test_plan_covers_the_row_and_follows_the_menu():
 def test_plan_for_the_named_workloads():
     # geometries measured best on MI355X for these shapes
     assert plan(8, 8192, 16384) == {"path": 2, "waves": 4, "chunks": 8, "grid": 8192}
-    assert plan(4, 2048, 7168, 2) == {"path": 2, "waves": 4, "chunks": 4, "grid": 2048}
+    assert plan(4, 2048, 7168, 2) == {"path": 3, "waves": 4, "chunks": 4, "grid": 256}
     assert plan(8, 128, 4096) == {"path": 2, "waves": 8, "chunks": 1, "grid": 128}
     assert plan(8, 64, 8192) == {"path": 2, "waves": 8, "chunks": 2, "grid": 64}
     assert plan(2, 16, 1024)["path"] == 2
@@ -157,6 +161,20 @@ def test_plan_row_per_wave_region():
     assert plan(8, 1023, 2048, 0, 128)["path"] == 2 and plan(8, 1024, 2048, 0, 128)["path"] == 1
 
 
+def test_plan_held_rows_region():
+    # held rows only where measured faster: <= 4 shards, 4096 <= hidden <= 8192, 6 to 16
+    # rows per CU, one batch per workgroup (LDS holds 11 rows of 7168, 9 of 8192)
+    assert plan(4, 1535, 7168, 2)["path"] == 2 and plan(4, 1536, 7168, 2)["path"] == 3
+    assert plan(4, 11 * 256, 7168, 2)["path"] == 3 and plan(4, 11 * 256 + 1, 7168, 2)["path"] == 2
+    assert plan(2, 9 * 256, 8192)["path"] == 3 and plan(2, 9 * 256 + 1, 8192)["path"] == 2
+    assert plan(4, 16 * 256, 4096)["path"] == 3 and plan(4, 16 * 256 + 1, 4096)["path"] == 2
+    assert plan(5, 2048, 7168)["path"] == 2
+    assert plan(4, 2048, 4088)["path"] != 3 and plan(4, 2048, 4096)["path"] == 3
+    assert plan(4, 2048, 8200)["path"] == 2
+    # the thresholds scale with the CU count
+    assert plan(4, 767, 7168, 2, 128)["path"] == 2 and plan(4, 768, 7168, 2, 128)["path"] == 3
+
+
 def test_path_override_forces_and_rejects():
     try:
         arf.arf_set_path_override(1)
@@ -167,7 +185,13 @@ def test_path_override_forces_and_rejects():
         assert plan(8, 8, 8192) == {"path": 2, "waves": 16, "chunks": 1, "grid": 8}
         with pytest.raises(arf.ArfError):
             plan(8, 8, 16384)
-        for bad in ((3, 0, 0), (0, 4, 0), (2, 3, 0), (2, 2, 0), (2, 4, 3), (1, 8, 0)):
+        arf.arf_set_path_override(3)
+        assert plan(8, 8192, 16384) == {"path": 3, "waves": 4, "chunks": 8, "grid": 256}
+        with pytest.raises(arf.ArfError):
+            plan(8, 8, 16392)            # more than 8 chunks per lane
+        arf.arf_set_path_override(3, 4, 4)
+        assert plan(8, 100, 4096) == {"path": 3, "waves": 4, "chunks": 4, "grid": 100}
+        for bad in ((4, 0, 0), (0, 4, 0), (2, 3, 0), (2, 2, 0), (2, 4, 3), (1, 8, 0), (3, 8, 0)):
             with pytest.raises(arf.ArfError):
                 arf.arf_set_path_override(*bad)
     finally:
