@@ -153,7 +153,79 @@ def parse():
                     help="skip the accumulation and token-slice variants")
     ap.add_argument("--secondary", default="c3",
                     help="second workload reported in the 'secondary' object ('' for none)")
+    ap.add_argument("--profile-variant", default=None,
+                    choices=["fused", "mxfp4", "acc_partial", "reduce_rows", "epilogue",
+                             "copy"],
+                    help="launch only this variant of the workload (warmup + steps times) "
+                         "and print its timing, for profiler runs; no contract line")
     return ap.parse_args()
+
+
+def profile_variant(args, w, run, stream):
+    """One variant of the workload on its own, for rocprofv3 runs: the fused call as
+    timed (fused), the MXFP4 copy in place of the fp8 one (mxfp4), accumulation in the
+    partial type (acc_partial), one rank's token slice of the reduce (reduce_rows), the
+    epilogue over gathered reduced values (epilogue), or the library's streaming copy of
+    exactly 1 GiB (copy: the calibration of the HBM byte counters)."""
+    import torch
+
+    import shard_reduce_residual_amd as arf
+
+    p, r, g, rout, nout, q, sc_out, sc_in = run.sets[0]
+    t, h, n = w.tokens, w.hidden, w.n_shards
+    mode = arf.ARF_QUANT_PER_TOKEN if w.quant == "per_token" else arf.ARF_QUANT_PER_TENSOR
+    quant = dict(quant_out=q, mode=mode, scale_in=sc_in, scale_out=sc_out) if w.quant else {}
+    v = args.profile_variant
+    if v == "copy":
+        one_gib = 1 << 30
+        src = torch.empty(one_gib, dtype=torch.uint8, device=rout.device)
+        dst = torch.empty(one_gib, dtype=torch.uint8, device=rout.device)
+
+        def fn():
+            arf.arf_stream_copy(dst, src, one_gib, stream=stream)
+        nbytes = 2 * one_gib
+    elif v == "fused":
+        fn, nbytes = run.step, w.algorithmic_bytes()
+    elif v == "acc_partial":
+        def fn():
+            arf.arf_fused_epilogue(p, r, g, w.eps, residual_out=rout, norm_out=nout,
+                                   accumulate=arf.ARF_ACC_PARTIAL, stream=stream, **quant)
+        nbytes = w.algorithmic_bytes()
+    elif v == "mxfp4":
+        q4 = torch.empty((t, h // 2), dtype=torch.uint8, device=rout.device)
+        s4 = torch.empty((t, h // 32), dtype=torch.uint8, device=rout.device)
+
+        def fn():
+            arf.arf_fused_epilogue(p, r, g, w.eps, residual_out=rout, norm_out=nout,
+                                   quant_out=q4, mode=arf.ARF_QUANT_MXFP4, scale_out=s4,
+                                   stream=stream)
+        nbytes = (w.with_tokens(t).algorithmic_bytes()
+                  - (t * h + 4 * t if w.quant == "per_token" else (t * h + 4 if w.quant else 0))
+                  + t * h // 2 + t * h // 32)
+    else:
+        sums = torch.empty((t, h), dtype=rout.dtype, device=rout.device)
+        arf.arf_reduce_rows(p, sums, stream=stream)
+        cnt = t // n + (1 if t % n else 0)
+        if v == "reduce_rows":
+            def fn():
+                arf.arf_reduce_rows(p, sums, row_begin=0, row_count=cnt, stream=stream)
+            nbytes = n * cnt * h * w.sp + cnt * h * w.sa
+        else:
+            def fn():
+                if w.quant:
+                    arf.arf_reduce_add_rmsnorm_quant(sums.view(1, t, h), r, g, w.eps, q, mode,
+                                                     scale_in=sc_in, scale_out=sc_out,
+                                                     residual_out=rout, norm_out=nout,
+                                                     stream=stream)
+                else:
+                    arf.arf_reduce_add_rmsnorm(sums.view(1, t, h), r, g, w.eps,
+                                               residual_out=rout, norm_out=nout, stream=stream)
+            nbytes = w.algorithmic_bytes() - n * t * h * w.sp + t * h * w.sa
+    ms = _events_ms(fn, stream, args.steps, args.warmup)
+    print(json.dumps({"variant": v, "workload": w.name, "launches": args.steps,
+                      "kernel_ms": round(ms, 5), "algorithmic_bytes": nbytes,
+                      "achieved_GBs": round(nbytes / (ms * 1e-3) / 1e9, 2)}), flush=True)
+    return 0
 
 
 def main():
@@ -179,6 +251,8 @@ def main():
     # workloads smaller than 1.5 GB rotate input/output sets so that the 256 MB Infinity
     # Cache cannot serve a launch (c0-c2 still fit in it: see decode_cold for those)
     run = Runner(w, dev, stream, sets=max(1, min(8, -(-1_500_000_000 // B))))
+    if args.profile_variant:
+        return profile_variant(args, w, run, stream)
     ms_per_step, kernel_ms = run.measure(args.steps, args.warmup)
     value = B / (ms_per_step * 1e-3) / 1e9
     achieved = B / (kernel_ms * 1e-3) / 1e9
@@ -197,6 +271,7 @@ def main():
         ms2, kms2 = run2.measure(steps2, max(args.warmup, 10))
         launch2 = percentiles_us(run2.distribution(steps2))
         mix2 = None if args.no_copy_probe else mix_probe(w2, run2, stream)
+        best2 = None if args.no_copy_probe else best_mix_probe(w2, run2, stream, mix2)
         del run2
         torch.cuda.empty_cache()
         secondary = {"workload": w2.name, "buffer_sets": sets, "steps": steps2,
@@ -208,9 +283,12 @@ def main():
                      "plan": arf.arf_get_plan(w2.n_shards, w2.tokens, w2.hidden,
                                               {"bf16": 0, "f16": 1, "f32": 2}[w2.partial_dtype]),
                      "traffic": read_traffic(w2.name),
-                     "mix_GBs": mix2,
-                     "frac_of_mix_ceiling": None if mix2 is None else
-                                            round(B2 / (kms2 * 1e-3) / 1e9 / mix2, 4)}
+                     "row_mix_GBs": mix2,
+                     "frac_of_row_mix_probe": None if mix2 is None else
+                                              round(B2 / (kms2 * 1e-3) / 1e9 / mix2, 4),
+                     "best_mix": best2,
+                     "frac_of_best_mix": None if best2 is None else
+                                         round(B2 / (kms2 * 1e-3) / 1e9 / best2["GBs"], 4)}
 
     cpu = None
     parity = None
@@ -257,8 +335,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "hbm_probes": probes,
-        "frac_of_copy_ceiling": None if probes is None else round(achieved / probes["copy_GBs"], 4),
-        "frac_of_mix_ceiling": None if probes is None else round(achieved / probes["mix_GBs"], 4),
+        "frac_of_best_mix": None if probes is None else round(achieved / probes["best_mix_GBs"], 4),
+        "frac_of_row_mix_probe": None if probes is None else round(achieved / probes["row_mix_GBs"], 4),
         "secondary": secondary,
         "variants": variants,
         "decode_cold": decode,
@@ -297,11 +375,46 @@ def mix_probe(w, run, stream, reps=20):
     return round((read_b + write_b) / (ms * 1e-3) / 1e9, 1)
 
 
+def best_mix_probe(w, run, stream, row_mix, reps=10):
+    """The workload's read/write mix with no arithmetic as its best pattern (GB/s): the
+    fastest of 1/32 .. 1/2 units per row (each unit reading its share before writing any)
+    and the one-unit-per-row probe (row_mix, measured already), rotating over the runner's
+    buffer sets like the timed launches."""
+    import torch
+
+    import shard_reduce_residual_amd as arf
+
+    n, t, h = w.n_shards, w.tokens, w.hidden
+    B = w.algorithmic_bytes()
+    alg_read = n * t * h * w.sp + t * h * w.sa + h * w.sa + (4 if w.quant == "per_tensor" else 0)
+    read_b = n * t * h * w.sp
+    write_b = (int(read_b * (B - alg_read) / alg_read) // 16) * 16
+    outs = [torch.empty(write_b, dtype=torch.uint8, device=run.sets[0][0].device)
+            for _ in run.sets]
+    best = {"GBs": row_mix, "units": t}
+    for units in sorted({max(1, t // d) for d in (32, 16, 8, 4, 2)}):
+        k = [0]
+
+        def one():
+            i = k[0] % len(run.sets)
+            k[0] += 1
+            arf.arf_stream_mix(outs[i], write_b, run.sets[i][0], read_b, units=units,
+                               stream=stream)
+
+        ms = _events_ms(one, stream, reps, 3)
+        gbs = round((read_b + write_b) / (ms * 1e-3) / 1e9, 1)
+        if gbs > best["GBs"]:
+            best = {"GBs": gbs, "units": units}
+    del outs
+    return best
+
+
 def hbm_probes(w, partials, stream, reps=10):
-    """HBM ceilings from streaming kernels with no arithmetic (GB/s): read only, write
-    only, a copy, and the workload's own mix -- reading the partials buffer and writing
-    a buffer in the workload's write:read ratio, in one unit per row (reads, then writes,
-    per unit), as the fused kernel does."""
+    """Streaming kernels with no arithmetic (GB/s): read only, write only, a copy, and the
+    workload's own read/write mix -- reading the partials buffer and writing a buffer in
+    the workload's write:read ratio -- once as one unit per row (reads, then writes, per
+    unit, as the fused kernel does: row_mix) and once as the best over 1/32 .. 1 units per
+    row (best_mix, the fastest pattern measured for this byte mix)."""
     import torch
 
     import shard_reduce_residual_amd as arf
@@ -342,9 +455,20 @@ def hbm_probes(w, partials, stream, reps=10):
     out["copy_GBs"] = round(2 * one_gib / t_c / 1e9, 1)
     t_m = timed(lambda: arf.arf_stream_mix(dst, mix_write, partials, read_b, units=t,
                                            stream=stream))
-    out["mix_GBs"] = round((read_b + mix_write) / t_m / 1e9, 1)
+    out["row_mix_GBs"] = round((read_b + mix_write) / t_m / 1e9, 1)
     out["mix_read_fraction"] = round(read_b / (read_b + mix_write), 4)
-    out["mix_units"] = t
+    out["row_mix_units"] = t
+    # the best pattern measured for this byte mix: fewer, larger units that each read all
+    # of their share before writing any (with every unit resident, the whole chip reads and
+    # then writes)
+    best = (out["row_mix_GBs"], t)   # one unit per row is one of the patterns
+    for units in sorted({max(1, t // d) for d in (32, 16, 8, 4, 2)}):
+        tu = timed(lambda: arf.arf_stream_mix(dst, mix_write, partials, read_b, units=units,
+                                              stream=stream))
+        gbs = round((read_b + mix_write) / tu / 1e9, 1)
+        if gbs > best[0]:
+            best = (gbs, units)
+    out["best_mix_GBs"], out["best_mix_units"] = best
     del dst
     return out
 

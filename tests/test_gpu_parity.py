@@ -145,12 +145,23 @@ def upload(w):
 
 
 def test_inputs_are_the_same_on_the_gpu_and_the_cpu():
-    # the counter-based generator gives the same bits on either device
+    # the counter-based generator gives the same bits on either device: c0..c3 whole, and
+    # the largest workload (generated whole on the GPU by the benchmark and the tests) in
+    # its first and last 64 rows of every shard, from the CPU row generator
     for key in ("c0", "c1", "c2", "c3"):
         w = workloads.WORKLOADS[key]
         say("generator %s cpu vs gpu" % w.name)
         for a, b in zip(workloads.generate(w, "cpu"), workloads.generate(w, DEV)):
             assert torch.equal(a, b.cpu()), w.name
+    w = workloads.WORKLOADS["c4"]
+    p, r, g = workloads.generate(w, DEV)
+    for b in (0, w.tokens - 64):
+        say("generator %s rows %d..%d cpu vs gpu" % (w.name, b, b + 64))
+        pc, rc, gc = workloads.generate_rows(w, b, 64, "cpu")
+        assert torch.equal(pc, p[:, b:b + 64].cpu()), b
+        assert torch.equal(rc, r[b:b + 64].cpu()), b
+        assert torch.equal(gc, g.cpu())
+    del p, r
 
 # ---- the five workloads --------------------------------------------------------------------
 

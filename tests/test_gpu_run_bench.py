@@ -35,7 +35,13 @@ def test_bench_prints_one_contract_line():
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
     sp = d["sample_parity"]
     assert sp["residual_bit_exact"] and sp["norm_max_ulp"] <= 1
+    # the probes: the kernel's own row-by-row mix, and the best pattern for the same byte
+    # mix, which the row-by-row probe cannot beat
+    hp = d["hbm_probes"]
+    assert hp["best_mix_GBs"] >= hp["row_mix_GBs"] > 0 and hp["best_mix_units"] >= 1
+    assert abs(d["frac_of_best_mix"] - rl["achieved"] / hp["best_mix_GBs"]) < 1e-3
     assert d["secondary"]["workload"] == "c2_n8_t64_h8192_bf16_fp8tensor"
+    assert d["secondary"]["best_mix"]["GBs"] > 0
     for key in ("c0_n2_t16_h1024_bf16", "c1_n8_t128_h4096_bf16",
                 "c2_n8_t64_h8192_bf16_fp8tensor"):
         assert d["variants"]["graph_replay"][key]["us_per_launch"] > 0

@@ -161,6 +161,32 @@ def test_gamma_one_gives_unit_rms():
     assert np.all(np.abs(rms2 - np.sqrt(m / (m + np.float32(eps)))) < 2.0 ** -8)
 
 
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+def test_gamma_one_unit_rms_exactly_on_exact_rows(act):
+    # Rows of +-1 and +-3 (40 and 24 of 64, random signs and places) times 2^k have the mean
+    # square exactly 4 * 4^k, so with eps = 0 the scale is exactly 2^-(k+1) and every output
+    # is +-0.5 or +-1.5, exact in bf16 and fp16: the output RMS must be 1 to the last bit
+    # (the 1e-5 bar with no rounding allowance). A mean over H-1 (a 1.6% larger scale), a
+    # root of the sum, or a mean of |x| instead of x^2 each move the outputs off +-0.5/+-1.5
+    # by whole ulps.
+    rng = np.random.default_rng(7)
+    h, rows = 64, []
+    for k in (-3, 0, 0, 4):
+        mag = np.concatenate([np.ones(40), 3.0 * np.ones(24)])
+        rng.shuffle(mag)
+        rows.append(mag * rng.choice([-1.0, 1.0], size=h) * 2.0 ** k)
+    x = np.array(rows)
+    p = _act_bits(x[None], act)               # one shard, residual zero: r = x exactly
+    r = _act_bits(np.zeros_like(x), act)
+    g1 = _act_bits(np.ones(h), act)
+    out = _run(p, r, g1, 0.0, act, act)
+    assert np.array_equal(out["residual_out"], _act_bits(x, act))
+    y = act_bits_to_f64(out["norm_out"], act)
+    assert np.array_equal(np.abs(y) * 2.0, np.abs(x) / np.abs(x).min(axis=1, keepdims=True))
+    rms = np.sqrt((y * y).mean(axis=1))
+    assert np.all(np.abs(rms - 1.0) < 1e-5) and np.all(rms == 1.0)
+
+
 def test_power_of_two_scaling_leaves_output_unchanged():
     w, p, r, g = _gen("c0")
     base = _run(p, r, g, 0.0, "bf16", "bf16")

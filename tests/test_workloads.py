@@ -55,3 +55,14 @@ def test_workload_recipe_moments_and_outliers():
     assert abs(p[:, :, mask].std().item() - 100.0) < 2.0
     assert abs(r.float().std().item() - 1.0) < 0.01
     assert 0.5 <= g.float().min().item() and g.float().max().item() <= 1.5
+
+
+def test_row_generator_matches_the_whole_generator():
+    # generate_rows gives exactly the rows of generate, outlier channels included
+    for key in ("c0", "c3"):
+        w = workloads.WORKLOADS[key].with_tokens(40)
+        p, r, g = workloads.generate(w, "cpu")
+        for b, c in ((0, 7), (13, 20), (39, 1)):
+            pr, rr, gr = workloads.generate_rows(w, b, c, "cpu")
+            assert torch.equal(pr, p[:, b:b + c]) and torch.equal(rr, r[b:b + c])
+            assert torch.equal(gr, g)

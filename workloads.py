@@ -158,23 +158,33 @@ def _store(x64: torch.Tensor, dtype) -> torch.Tensor:
     return x if dtype == torch.float32 else x.to(dtype)
 
 
-def generate(w: Workload, device="cpu"):
-    """Return (partials [N][T][H], residual [T][H], gamma [H]) as torch tensors on
-    ``device`` in the workload's types; the same values on every device."""
+def generate_rows(w: Workload, row_begin: int, row_count: int, device="cpu"):
+    """Rows row_begin .. row_begin+row_count-1 of the workload: (partials [N][count][H],
+    residual [count][H], gamma [H]) on ``device``, the same values that ``generate`` puts in
+    those rows (element (r, t, i) of the partials is element (r*T + t)*H + i of stream 0)."""
     device = torch.device(device)
     pdt, adt = TORCH_DTYPES[w.partial_dtype], TORCH_DTYPES[w.act_dtype]
     n, t, h = w.n_shards, w.tokens, w.hidden
-    partials = torch.empty((n, t, h), dtype=pdt, device=device)
+    assert 0 <= row_begin and row_begin + row_count <= t
+    partials = torch.empty((n, row_count, h), dtype=pdt, device=device)
     cols = outlier_channels(w).to(device)
     for r in range(n):  # one shard at a time bounds the fp64 temporaries
-        x = normal(w.seed, 0, r * t * h, t * h, device).view(t, h).mul_(w.partial_std)
+        x = normal(w.seed, 0, (r * t + row_begin) * h, row_count * h,
+                   device).view(row_count, h).mul_(w.partial_std)
         if cols.numel():
             x[:, cols] *= w.outlier_scale
         partials[r].copy_(_store(x, pdt))
         del x
-    res = _store(normal(w.seed, 1, 0, t * h, device).view(t, h) * w.residual_std, adt)
+    res = _store(normal(w.seed, 1, row_begin * h, row_count * h,
+                        device).view(row_count, h) * w.residual_std, adt)
     gamma = _store(uniform(w.seed, 2, 0, h, device) + 0.5, adt)
     return partials, res, gamma
+
+
+def generate(w: Workload, device="cpu"):
+    """Return (partials [N][T][H], residual [T][H], gamma [H]) as torch tensors on
+    ``device`` in the workload's types; the same values on every device."""
+    return generate_rows(w, 0, w.tokens, device)
 
 
 def to_bits(x: torch.Tensor):
