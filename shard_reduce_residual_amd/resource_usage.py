@@ -1,5 +1,5 @@
 """On-chip budget of the kernels the launch plan picks: registers, LDS, scratch and the
-resulting occupancy, read from the code-object metadata of this build (hipcc -S of the
+resulting occupancy, read from the code-object metadata of the current sources (hipcc -S of the
 instantiation units; nothing is launched, no GPU is needed).
 
     python -m shard_reduce_residual_amd.resource_usage [--cus 256]
