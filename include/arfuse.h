@@ -22,9 +22,16 @@
  * scale max|y|/448 computed here.
  *
  * Conventions for every entry point below:
- *   - Buffers are DEVICE pointers owned by the caller; the library allocates nothing,
- *     keeps no state between calls (apart from a per-device compute-unit count and the
- *     test-only override below) and never synchronises.
+ *   - Buffers are DEVICE pointers owned by the caller; the library allocates nothing and
+ *     never synchronises. Its only state is a per-device compute-unit count, the test-only
+ *     override below, and the row-claim counters of large launches: a file-scope device
+ *     array of 256 counters (64 KiB per device, no allocation), one per stream on first use
+ *     and for the life of the process. A launch with claimed rows leaves its counter at 0.
+ *     Calls on one stream run one after another and share its counter; calls on different
+ *     streams never share one. A call enqueued under stream capture, on the per-thread
+ *     default stream, on a stream of another device, or once every counter belongs to
+ *     another stream, takes the same kernel with rows by workgroup index instead (the same
+ *     outputs, bit for bit).
  *   - `stream` is a hipStream_t (NULL = the legacy default stream). On ARF_OK one kernel
  *     has been enqueued on it (none when tokens == 0; several, in row order, when a
  *     one-row-per-workgroup or one-row-per-wavefront grid would exceed the 2^32 - 1
@@ -44,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ARF_VERSION 200 /* 0.2.0 */
+#define ARF_VERSION 300 /* 0.3.0 */
 
 /* Element types (arguments typed int32_t take these values). */
 #define ARF_BF16 0
@@ -197,9 +204,13 @@ int32_t arf_version(void);
  * the current device's compute-unit count and LDS size are queried, which may return
  * ARF_ERR_HIP). out[0] = path: 1 row per wavefront, 2 row per workgroup, 3 held rows (one
  * workgroup per compute unit reads a batch of rows, keeping each row's rounded residual in
- * LDS, then writes their outputs); out[1] = wavefronts per workgroup; out[2] = 16-byte
- * chunks (8 elements) per lane; out[3] = workgroups in the grid (as an unsigned 32-bit
- * value). Honours arf_set_path_override.
+ * LDS, then writes their outputs), 4 row per workgroup with the rows past the first two
+ * workgroups per compute unit claimed from a counter in the order the workgroups start
+ * (two workgroups per compute unit; a call that may not claim, see the conventions above,
+ * runs path 2 with a grid of one workgroup per row); out[1] = wavefronts per workgroup;
+ * out[2] = 16-byte chunks (8 elements) per lane; out[3] = workgroups in the grid (as an
+ * unsigned 32-bit value; path 4: the rows plus max(64, rows/16) workgroups that find no
+ * row). Honours arf_set_path_override.
  */
 arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
                         int32_t partial_dtype, int32_t num_cus, int32_t* out);
@@ -207,9 +218,11 @@ arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
 /*
  * TEST AND TUNING ONLY; process-wide, not to be changed while other threads call the
  * library. path 0 = automatic (the other two arguments must be 0); 1 = one row per
- * wavefront; 2 = one row per workgroup; 3 = held rows (4 wavefronts; rows of up to 16384
- * elements; arf_reduce_rows keeps its automatic plan). waves_per_block (path 2: 4, 8 or
- * 16; paths 1 and 3: 0 or 4) and chunks_per_lane (1, 2, 4 or 8) force the geometry when
+ * wavefront; 2 = one row per workgroup, rows by workgroup index; 3 = held rows (4
+ * wavefronts; rows of up to 16384 elements; arf_reduce_rows keeps its automatic plan);
+ * 4 = one row per workgroup with EVERY row claimed from the stream's counter (where a call
+ * may claim; a grid beyond one dispatch runs path 2). waves_per_block (paths 2 and 4: 4, 8
+ * or 16; paths 1 and 3: 0 or 4) and chunks_per_lane (1, 2, 4 or 8) force the geometry when
  * non-zero. A forced geometry that cannot cover a call's hidden size makes that call return
  * ARF_ERR_VALUE. Returns ARF_ERR_VALUE for values outside these sets.
  */

@@ -65,6 +65,11 @@ struct Params {
     int32_t acc_partial;       // round every partial sum to the partial type
     int32_t reduce_only;       // store the reduced value and stop
     int32_t held_rows;         // held-row kernel: rows a workgroup holds at once (K)
+    // Row claims (one row per workgroup only): workgroups with index >= claim_static take
+    // their row from *claim in the order they start; NULL: row = row_begin + workgroup index.
+    uint32_t* claim;           // counter, 0 at launch; the launch leaves it at 0
+    int64_t claim_static;      // workgroups below this index keep row_begin + index
+    uint32_t claim_count;      // workgroups that claim (gridDim.x - claim_static)
 };
 
 struct ActBF16 {};
@@ -364,6 +369,25 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
     } else {
         row = p.row_begin + (int64_t)blockIdx.x;
         gl = threadIdx.x;
+        if (p.claim && (int64_t)blockIdx.x >= p.claim_static) {
+            // Past the static prefix, rows go to workgroups in the order they start: the
+            // rows in flight then stay one compact window of the launch however far the
+            // XCDs drift apart, and a faster XCD takes more rows. One relaxed device-scope
+            // increment per workgroup; the launch's last increment returns the counter to 0
+            // for the next launch on the same stream. The grid has claim_count workgroups
+            // past the prefix, more than the rows left: the surplus finds no row and exits.
+            __shared__ int64_t s_row;
+            if (threadIdx.x == 0) {
+                const uint32_t c = __hip_atomic_fetch_add(p.claim, 1u, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+                if (c == p.claim_count - 1u)
+                    __hip_atomic_store(p.claim, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_row = p.claim_static + (int64_t)c;
+            }
+            __syncthreads();
+            row = p.row_begin + s_row;
+            if (row >= p.row_end) return;   // uniform: the whole workgroup leaves
+        }
     }
 
     const uint32_t H = (uint32_t)p.hidden;
@@ -813,18 +837,20 @@ void fused_held_rows(Params p) {
     }
 }
 
-// Host-side launcher for one instantiation; returns the launch's own status.
+// Host-side launcher for one instantiation; returns the launch's own status. `lds` bytes of
+// dynamic LDS are reserved per workgroup (the kernel does not use them): a reservation caps
+// how many workgroups share a compute unit.
 template <class PT, class AT, int N, int C, int WAVES, bool ROW_PER_WAVE, int DEPTH = 2>
-hipError_t launch_fused(const Params& p, uint32_t grid, hipStream_t stream) {
+hipError_t launch_fused(const Params& p, uint32_t grid, uint32_t lds, hipStream_t stream) {
     Params arg = p;
     void* args[] = {&arg};
     return hipLaunchKernel(
         reinterpret_cast<const void*>(
             &fused_reduce_add_rmsnorm<PT, AT, N, C, WAVES, ROW_PER_WAVE, DEPTH>),
-        dim3(grid), dim3(WAVES * 64), args, 0, stream);
+        dim3(grid), dim3(WAVES * 64), args, lds, stream);
 }
 
-typedef hipError_t (*launch_fn)(const Params&, uint32_t, hipStream_t);
+typedef hipError_t (*launch_fn)(const Params&, uint32_t, uint32_t, hipStream_t);
 
 // Held-row kernel launcher: `lds` bytes of dynamic LDS per workgroup.
 template <class PT, class AT, int N, int C, int WAVES>

@@ -3,11 +3,14 @@
 // quantiser's conversion alone, and a streaming copy for the HBM ceiling).
 //
 // Every argument is validated before the first HIP call. The only device queries are
-// hipGetDevice and the compute-unit count (cached per device).
+// hipGetDevice, the compute-unit count and LDS size (cached per device), and, for calls
+// whose rows are claimed from a counter, the stream's device and capture status.
+#include <algorithm>
 #include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "arfuse.h"
 #include "arfuse_table.hpp"
@@ -33,18 +36,78 @@ std::atomic<int> g_lds_bytes[kMaxDevices];  // LDS bytes a workgroup may use; 0 
 std::atomic<int> g_path{0}, g_waves{0}, g_chunks{0};
 
 struct Plan {
-    int path;      // 1 row per wavefront, 2 row per workgroup, 3 held rows
+    int path;      // 1 row per wavefront, 2 row per workgroup, 3 held rows, 4 row per
+                   // workgroup with rows claimed in start order
     int waves;     // wavefronts per workgroup
     int chunks;    // 16-byte chunks per lane
     uint32_t grid; // workgroups
     int held;      // held-row kernel: rows per workgroup and phase
-    uint32_t lds;  // held-row kernel: dynamic LDS bytes per workgroup
+    uint32_t lds;  // dynamic LDS bytes per workgroup (held rows; the occupancy cap of path 4)
+    int64_t claim_static;   // path 4: workgroups that keep the row of their index
+    uint32_t claim_count;   // path 4: workgroups that claim a row
 };
 
 struct DeviceInfo {
     int cus;       // compute units
     int lds;       // LDS bytes one workgroup may allocate
+    int index;     // device ordinal (-1 when the caller gave the CU count)
 };
+
+// ---- row-claim counters -------------------------------------------------------------------
+//
+// Path 4 hands rows to workgroups from a device counter that every launch returns to 0. The
+// counters are this file-scope array, one 256-byte line each (so no two share a cache line
+// or an atomic unit's queue), on every device the library runs on; nothing is allocated.
+// A counter belongs to one stream: calls on one stream run one after another, so they may
+// share it, and calls on different streams, which may overlap, never do. Calls that must
+// not claim (see claim_counter) take the same kernel with rows by workgroup index.
+constexpr int kClaimSlots = 256;
+constexpr int kSlotWords = 64;
+static __device__ __align__(256) uint32_t scratch[kClaimSlots * kSlotWords];
+
+struct ClaimTable {
+    std::mutex mu;
+    uint32_t* base[kMaxDevices] = {};    // device address of `scratch` (hipGetSymbolAddress)
+    bool unusable[kMaxDevices] = {};     // the symbol address could not be obtained
+    uintptr_t owner[kMaxDevices][kClaimSlots] = {};   // stream handle + 1; 0 = free
+};
+ClaimTable g_claims;
+
+// The counter of `stream` on device `dev`, or NULL when the call must not claim rows:
+//  * the stream is being captured: a captured graph may be replayed on another stream;
+//  * the per-thread default stream: one handle stands for a different stream per thread;
+//  * the stream belongs to another device than the current one;
+//  * every slot of the device belongs to another stream, or the symbol's address could not
+//    be obtained.
+// A slot, once given to a stream handle, stays with it for the life of the process.
+uint32_t* claim_counter(int dev, void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    if (dev < 0 || dev >= kMaxDevices || st == hipStreamPerThread) return nullptr;
+    if (st) {
+        hipDevice_t sd = -1;
+        if (hipStreamGetDevice(st, &sd) != hipSuccess || sd != dev) return nullptr;
+    }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_claims.mu);
+    if (!g_claims.base[dev]) {
+        if (g_claims.unusable[dev]) return nullptr;
+        void* ptr = nullptr;   // the current device is `dev`: its copy of the array
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            g_claims.unusable[dev] = true;
+            return nullptr;
+        }
+        g_claims.base[dev] = static_cast<uint32_t*>(ptr);
+    }
+    const uintptr_t key = (uintptr_t)stream + 1;
+    for (int i = 0; i < kClaimSlots; ++i) {
+        uintptr_t& o = g_claims.owner[dev][i];
+        if (o == 0) o = key;
+        if (o == key) return g_claims.base[dev] + (size_t)i * kSlotWords;
+    }
+    return nullptr;
+}
 
 // Held-row kernel geometry: 4 wavefronts, one workgroup per compute unit, each holding up to
 // as many rows as its LDS takes (the row's residual plus 12 bytes per wavefront for the
@@ -96,6 +159,17 @@ bool held_plan(int64_t rows, int32_t hidden, const DeviceInfo& dev, int chunks, 
 //    launch's reads, then its writes: 2-10% faster (3% for 4 fp32 shards of 2048 x 7168). With more shards, other
 //    row sizes, several batches, or the per-token scale's extra pass over the held rows, it
 //    was slower than one row per workgroup.
+//  * rows claimed in start order (path 4, the same kernel as path 2) where a sweep of 32
+//    shapes (1-16 shards, hidden 4096-16384, 1024-16384 tokens, bf16 and fp32 partials)
+//    measured it faster: 4 wavefronts per row, and either at least 16 rows per compute unit
+//    with at least 128 KiB of traffic per row, or at least 8 rows per compute unit with at
+//    least 256 KiB per row: 1-8% faster (8 shards of 8192 x 16384 with per-token fp8:
+//    512-528 -> 481-487 us). With less traffic per row the launch claims rows faster than
+//    one counter serves them (beyond ~50 per microsecond), and with fewer rows per compute
+//    unit there is little drift to correct; there it was up to 8% slower. Two workgroups
+//    per compute unit (an LDS reservation caps them) measured faster than three with claims
+//    on every shape; the first two workgroups per compute unit keep their own row, so the
+//    launch's first wave of workgroups does not queue on the counter at once.
 bool held_wins(int64_t tokens, int32_t hidden, int n, int quant, const DeviceInfo& dev,
                Plan* pl) {
     if (n > 4 || hidden < 4096 || hidden > 8192 || quant != arf::kQuantNone ||
@@ -108,19 +182,35 @@ bool held_wins(int64_t tokens, int32_t hidden, int n, int quant, const DeviceInf
     return true;
 }
 
-arf_status make_plan(int64_t tokens, int32_t hidden, int n, int quant, const DeviceInfo& dev,
-                     bool reduce_only, Plan* pl) {
+// The claim rule of the plan (path 4), from the launch-geometry notes above.
+bool claim_wins(int64_t tokens, int64_t row_bytes, int waves, const DeviceInfo& dev) {
+    if (waves != 4) return false;
+    return (tokens >= 16LL * dev.cus && row_bytes >= 128 * 1024) ||
+           (tokens >= 8LL * dev.cus && row_bytes >= 256 * 1024);
+}
+
+// Static LDS of the fused kernel (per-wavefront partial sums and maxima, the claimed row),
+// left free beside the path-4 reservation so that exactly two workgroups fit a compute unit.
+constexpr int kStaticLdsSlack = 2048;
+
+// row_bytes: HBM traffic of one row (partials, residual, outputs), for the claim rule.
+arf_status make_plan(int64_t tokens, int32_t hidden, int n, int quant, int64_t row_bytes,
+                     const DeviceInfo& dev, bool reduce_only, Plan* pl) {
     const int hc = hidden / 8;
     const int num_cus = dev.cus;
     int path = g_path.load(), waves = g_waves.load(), chunks = g_chunks.load();
     pl->held = 0;
     pl->lds = 0;
+    pl->claim_static = 0;
+    pl->claim_count = 0;
     if (path == 3) {
         // the held-row kernel has no reduce-only form: such calls take the default plan
         if (!reduce_only) return held_plan(tokens, hidden, dev, chunks, pl) ? ARF_OK : ARF_ERR_VALUE;
         path = waves = chunks = 0;
     }
     if (path == 0 && !reduce_only && held_wins(tokens, hidden, n, quant, dev, pl)) return ARF_OK;
+    const bool forced_claims = path == 4;
+    bool claims = forced_claims;
     if (path == 0) {
         waves = chunks = 0;
         const bool many_rows = tokens >= 2LL * num_cus;
@@ -131,6 +221,7 @@ arf_status make_plan(int64_t tokens, int32_t hidden, int n, int quant, const Dev
             waves = many_rows ? 4 : 8;
             if (hc > waves * 64 * 8) waves = 16;
             chunks = pow2_at_least(div_up(hc, waves * 64));
+            claims = claim_wins(tokens, row_bytes, waves, dev);
         }
     }
     if (path == 1) {
@@ -139,8 +230,8 @@ arf_status make_plan(int64_t tokens, int32_t hidden, int n, int quant, const Dev
         if (chunks > 8 || 64 * chunks < hc) return ARF_ERR_VALUE;
         pl->grid = (uint32_t)((tokens + 3) / 4);
     } else {
-        if (waves == 0 && chunks == 0) {
-            waves = 4;
+        if (waves == 0 && chunks == 0) {   // forced path, free geometry: as the plan's
+            waves = hc > 4 * 64 * 8 ? 16 : 4;
             chunks = pow2_at_least(div_up(hc, waves * 64));
         } else if (waves == 0) {
             for (waves = 4; waves < 16 && waves * 64 * chunks < hc; waves *= 2) {}
@@ -149,6 +240,21 @@ arf_status make_plan(int64_t tokens, int32_t hidden, int n, int quant, const Dev
         }
         if (chunks > 8 || waves * 64 * chunks < hc) return ARF_ERR_VALUE;
         pl->grid = (uint32_t)tokens;
+        path = 2;
+        if (claims) {
+            // forced (tests): every row is claimed; planned: the first two workgroups per
+            // compute unit keep their row. One claiming workgroup per 16 rows (at least 64)
+            // beyond the rows is the slack that lets a faster XCD take more rows.
+            const int64_t first = forced_claims ? 0 : std::min<int64_t>(tokens, 2LL * num_cus);
+            const int64_t grid = tokens + std::max<int64_t>(64, tokens / 16);
+            if (grid * 64 * waves <= (int64_t)UINT32_MAX) {   // one dispatch, else path 2
+                path = 4;
+                pl->claim_static = first;
+                pl->claim_count = (uint32_t)(grid - first);
+                pl->grid = (uint32_t)grid;
+                pl->lds = (uint32_t)((dev.lds - kStaticLdsSlack) / 2);
+            }
+        }
     }
     pl->path = path;
     pl->waves = waves;
@@ -195,7 +301,7 @@ arf_status device_info(DeviceInfo* info) {
         const int c = g_cu_count[dev].load(std::memory_order_relaxed);
         const int l = g_lds_bytes[dev].load(std::memory_order_relaxed);
         if (c > 0 && l > 0) {
-            *info = DeviceInfo{c, l};
+            *info = DeviceInfo{c, l, dev};
             return ARF_OK;
         }
     }
@@ -210,7 +316,7 @@ arf_status device_info(DeviceInfo* info) {
         g_cu_count[dev].store(c, std::memory_order_relaxed);
         g_lds_bytes[dev].store(l, std::memory_order_relaxed);
     }
-    *info = DeviceInfo{c, l};
+    *info = DeviceInfo{c, l, dev};
     return ARF_OK;
 }
 
@@ -320,9 +426,21 @@ arf_status run(Call c, void* stream) {
     if (st != ARF_OK || c.row_count == 0) return st;
     DeviceInfo dev;
     if ((st = device_info(&dev)) != ARF_OK) return st;
+    const int64_t sp = c.pdt == ARF_F32 ? 4 : 2;
+    const int64_t qbytes = c.quant == arf::kQuantMx     ? c.hidden / 2 + c.hidden / 32
+                           : c.quant != arf::kQuantNone ? c.hidden
+                                                        : 0;
+    const int64_t row_bytes = (int64_t)c.n * c.hidden * sp + 2LL * c.hidden * 3 + qbytes;
     Plan pl;
-    if ((st = make_plan(c.row_count, c.hidden, c.n, c.quant, dev, c.reduce_only, &pl)) != ARF_OK)
+    if ((st = make_plan(c.row_count, c.hidden, c.n, c.quant, row_bytes, dev, c.reduce_only,
+                        &pl)) != ARF_OK)
         return st;
+    uint32_t* counter = pl.path == 4 ? claim_counter(dev.index, stream) : nullptr;
+    if (pl.path == 4 && !counter) {   // the same kernel with rows by workgroup index
+        pl.path = 2;
+        pl.grid = (uint32_t)c.row_count;
+        pl.lds = 0;
+    }
     launch_fn fn = nullptr;
     held_launch_fn hfn = nullptr;
     if (pl.path == 3) hfn = lookup_held(c.pdt, c.adt, c.n, pl.chunks);
@@ -347,8 +465,17 @@ arf_status run(Call c, void* stream) {
     p.acc_partial = c.acc == ARF_ACC_PARTIAL;
     p.reduce_only = c.reduce_only;
     p.held_rows = pl.held;
+    p.claim = nullptr;
+    p.claim_static = 0;
+    p.claim_count = 0;
     if (hfn)   // at most one workgroup per compute unit, looping over its rows
         return hfn(p, pl.grid, pl.lds, (hipStream_t)stream) == hipSuccess ? ARF_OK : ARF_ERR_HIP;
+    if (pl.path == 4) {   // one dispatch (the plan checked its size)
+        p.claim = counter;
+        p.claim_static = pl.claim_static;
+        p.claim_count = pl.claim_count;
+        return fn(p, pl.grid, pl.lds, (hipStream_t)stream) == hipSuccess ? ARF_OK : ARF_ERR_HIP;
+    }
     // One dispatch covers at most 2^32 - 1 work-items: a grid that would exceed that is
     // split into consecutive row ranges, one kernel each, enqueued in row order.
     const int64_t threads = pl.path == 1 ? 256 : 64LL * pl.waves;
@@ -359,7 +486,7 @@ arf_status run(Call c, void* stream) {
         p.row_begin = b;
         p.row_end = end - b < max_rows ? end : b + max_rows;
         const uint32_t grid = (uint32_t)((p.row_end - b + rows_per_wg - 1) / rows_per_wg);
-        if (fn(p, grid, (hipStream_t)stream) != hipSuccess) return ARF_ERR_HIP;
+        if (fn(p, grid, 0, (hipStream_t)stream) != hipSuccess) return ARF_ERR_HIP;
     }
     return ARF_OK;
 }
@@ -534,13 +661,15 @@ arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
         return ARF_ERR_SHAPE;
     if (partial_dtype != ARF_BF16 && partial_dtype != ARF_F16 && partial_dtype != ARF_F32)
         return ARF_ERR_DTYPE;
-    DeviceInfo dev{num_cus, kPlanLdsBytes};
+    DeviceInfo dev{num_cus, kPlanLdsBytes, -1};
     if (num_cus <= 0) {
         arf_status st = device_info(&dev);
         if (st != ARF_OK) return st;
     }
+    const int64_t row_bytes = (int64_t)n_shards * hidden * (partial_dtype == ARF_F32 ? 4 : 2) +
+                              2LL * hidden * 3;
     Plan pl;
-    arf_status st = make_plan(tokens, hidden, n_shards, arf::kQuantNone, dev, false, &pl);
+    arf_status st = make_plan(tokens, hidden, n_shards, arf::kQuantNone, row_bytes, dev, false, &pl);
     if (st != ARF_OK) return st;
     out[0] = pl.path;
     out[1] = pl.waves;
@@ -551,13 +680,14 @@ arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
 
 arf_status arf_set_path_override(int32_t path, int32_t waves_per_block,
                                  int32_t chunks_per_lane) {
-    if (path < 0 || path > 3) return ARF_ERR_VALUE;
+    if (path < 0 || path > 4) return ARF_ERR_VALUE;
     if (path == 0 && (waves_per_block || chunks_per_lane)) return ARF_ERR_VALUE;
     if ((path == 1 || path == 3) && waves_per_block && waves_per_block != 4) return ARF_ERR_VALUE;
-    if (path == 2 && waves_per_block && !in_menu_w(waves_per_block)) return ARF_ERR_VALUE;
+    if ((path == 2 || path == 4) && waves_per_block && !in_menu_w(waves_per_block))
+        return ARF_ERR_VALUE;
     if (chunks_per_lane && !in_menu_c(chunks_per_lane)) return ARF_ERR_VALUE;
     g_path.store(path);
-    g_waves.store(path == 2 ? waves_per_block : 0);   // paths 1 and 3 always use 4
+    g_waves.store(path == 2 || path == 4 ? waves_per_block : 0);   // paths 1 and 3 use 4
     g_chunks.store(chunks_per_lane);
     return ARF_OK;
 }

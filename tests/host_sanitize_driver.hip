@@ -130,14 +130,28 @@ int main() {
                     int32_t o[4];
                     if (arf_get_plan(n, t, h, ARF_BF16, cus, o) != ARF_OK) { EXPECT(false); continue; }
                     const int64_t lanes = o[0] == 1 ? 64 : 64 * (int64_t)o[1];
-                    EXPECT(o[0] == 1 || o[0] == 2 || (o[0] == 3 && n <= 4));
+                    EXPECT(o[0] == 1 || o[0] == 2 || (o[0] == 3 && n <= 4) || o[0] == 4);
                     EXPECT(o[2] == 1 || o[2] == 2 || o[2] == 4 || o[2] == 8);
                     EXPECT(o[0] == 2 ? (o[1] == 4 || o[1] == 8 || o[1] == 16) : o[1] == 4);
                     EXPECT(lanes * o[2] * 8 >= h);
                     // held rows: one workgroup per compute unit, the whole launch in one batch
-                    // of at most 160 KiB of LDS per workgroup
-                    const int64_t g = o[0] == 1 ? (t + 3) / 4 : (o[0] == 2 ? t : (t < cus ? t : cus));
+                    // of at most 160 KiB of LDS per workgroup; claimed rows: the rows plus
+                    // max(64, rows/16) in one dispatch
+                    const int64_t surplus = t / 16 > 64 ? t / 16 : 64;
+                    const int64_t g = o[0] == 1 ? (t + 3) / 4
+                                      : o[0] == 2 ? t
+                                      : o[0] == 4 ? t + surplus
+                                                  : (t < cus ? t : cus);
                     EXPECT((int64_t)(uint32_t)o[3] == g);
+                    if (o[0] == 4) {
+                        const int64_t row_bytes = (int64_t)n * h * 2 + 6LL * h;
+                        EXPECT((t >= 16LL * cus && row_bytes >= 128 * 1024) ||
+                               (t >= 8LL * cus && row_bytes >= 256 * 1024));
+                        EXPECT(g * 256 <= (int64_t)UINT32_MAX);
+                    }
+                    // every launch of one row per workgroup or wavefront fits the work-item
+                    // limit of one dispatch, or is split by the caller into row ranges
+                    if (o[0] != 2 && o[0] != 1) EXPECT((int64_t)(uint32_t)o[3] * lanes <= (int64_t)UINT32_MAX);
                     if (o[0] == 3) {
                         EXPECT(t >= 6LL * cus && t <= 16LL * cus && h >= 4096 && h <= 8192);
                         EXPECT(div_up_i64(t, cus) * (2LL * h + 48) <= 160 * 1024);
@@ -166,16 +180,32 @@ int main() {
     EXPECT(arf_set_path_override(3, 4, 2) == ARF_OK);
     EXPECT(arf_get_plan(8, 100, 4096, ARF_BF16, 256, o) == ARF_OK && o[0] == 3 && o[2] == 2);
     EXPECT(arf_get_plan(8, 100, 4104, ARF_BF16, 256, o) == ARF_ERR_VALUE);
-    const int bad[][3] = {{4, 0, 0}, {-1, 0, 0}, {0, 4, 0}, {0, 0, 2}, {1, 8, 0}, {2, 3, 0}, {2, 4, 3}, {2, 32, 1}, {3, 8, 0}, {3, 0, 3}};
+    // claimed rows forced: every row claimed, any row count; beyond one dispatch, path 2
+    EXPECT(arf_set_path_override(4, 0, 0) == ARF_OK);
+    EXPECT(arf_get_plan(8, 100, 4096, ARF_BF16, 256, o) == ARF_OK && o[0] == 4 && o[1] == 4 && o[2] == 2 && o[3] == 164);
+    EXPECT(arf_get_plan(8, 0, 4096, ARF_BF16, 256, o) == ARF_OK && o[0] == 4 && o[3] == 64);
+    EXPECT(arf_get_plan(8, (int64_t(1) << 31) - 1, 4096, ARF_BF16, 256, o) == ARF_OK && o[0] == 2);
+    EXPECT(arf_get_plan(8, 100, 18016, ARF_BF16, 256, o) == ARF_OK && o[0] == 4 && o[1] == 16 && o[2] == 4);
+    EXPECT(arf_set_path_override(2, 0, 0) == ARF_OK);
+    EXPECT(arf_get_plan(8, 100, 65536, ARF_BF16, 256, o) == ARF_OK && o[0] == 2 && o[1] == 16 && o[2] == 8);
+    EXPECT(arf_set_path_override(4, 0, 0) == ARF_OK);
+    EXPECT(arf_set_path_override(4, 16, 8) == ARF_OK);
+    EXPECT(arf_get_plan(3, 100, 65536, ARF_BF16, 256, o) == ARF_OK && o[0] == 4 && o[1] == 16 && o[2] == 8);
+    EXPECT(arf_get_plan(3, 100, 65544, ARF_BF16, 256, o) == ARF_ERR_SHAPE);
+    const int bad[][3] = {{5, 0, 0}, {-1, 0, 0}, {0, 4, 0}, {0, 0, 2}, {1, 8, 0}, {2, 3, 0}, {2, 4, 3}, {2, 32, 1}, {3, 8, 0}, {3, 0, 3}, {4, 2, 0}, {4, 0, 3}};
     for (const auto& v : bad) EXPECT(arf_set_path_override(v[0], v[1], v[2]) == ARF_ERR_VALUE);
     EXPECT(arf_set_path_override(0, 0, 0) == ARF_OK);
-    EXPECT(arf_get_plan(8, 8192, 16384, ARF_BF16, 256, o) == ARF_OK && o[0] == 2 && o[1] == 4 && o[2] == 8);
+    EXPECT(arf_get_plan(8, 8192, 16384, ARF_BF16, 256, o) == ARF_OK && o[0] == 4 && o[1] == 4 && o[2] == 8 && o[3] == 8704);
+    EXPECT(arf_get_plan(8, 2047, 16384, ARF_BF16, 256, o) == ARF_OK && o[0] == 2);
+    EXPECT(arf_get_plan(8, 4096, 8192, ARF_BF16, 256, o) == ARF_OK && o[0] == 4);
+    EXPECT(arf_get_plan(8, 8192, 4096, ARF_BF16, 256, o) == ARF_OK && o[0] == 2);
+    EXPECT(arf_get_plan(4, 8192, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 4 && o[3] == 8704);
     // held rows by default only in their measured range
     EXPECT(arf_get_plan(4, 2048, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 3 && o[2] == 4 && o[3] == 256);
     EXPECT(arf_get_plan(8, 2048, 7168, ARF_BF16, 256, o) == ARF_OK && o[0] == 2);
     EXPECT(arf_get_plan(4, 1535, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 2);
     EXPECT(arf_get_plan(4, 1536, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 3);
-    EXPECT(arf_get_plan(4, 4096, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 2);   // two batches
+    EXPECT(arf_get_plan(4, 4096, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 4);   // two batches: claimed rows
     EXPECT(arf_get_plan(2, 4096, 4096, ARF_BF16, 256, o) == ARF_OK && o[0] == 3);
     EXPECT(arf_get_plan(2, 4096, 4088, ARF_BF16, 256, o) == ARF_OK && o[0] != 3);
     EXPECT(arf_get_plan(2, 4097, 4096, ARF_BF16, 256, o) == ARF_OK && o[0] != 3);

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert arf.arf_version() == 200
+    assert arf.arf_version() == 300
     for code, name in enumerate(arf.STATUS):
         assert arf.arf_status_string(code).startswith(name)
     assert "unknown" in arf.arf_status_string(99)
@@ -128,6 +128,9 @@ def test_plan_covers_the_row_and_follows_the_menu():
                         assert p["waves"] == 4 and p["grid"] == (t + 3) // 4
                     elif p["path"] == 2:
                         assert p["waves"] in (4, 8, 16) and p["grid"] == t
+                    elif p["path"] == 4:   # claimed rows: the rows plus the surplus
+                        assert p["waves"] == 4 and p["grid"] == t + max(64, t // 16)
+                        assert t >= 8 * 256
                     else:   # held rows: one workgroup per CU, one batch of rows each
                         assert p["path"] == 3 and n <= 4 and p["waves"] == 4
                         assert p["grid"] == min(t, 256) and 6 * 256 <= t <= 16 * 256
@@ -137,12 +140,13 @@ def test_plan_covers_the_row_and_follows_the_menu():
 
 def test_plan_for_the_named_workloads():
     # geometries measured best on MI355X for these shapes
-    assert plan(8, 8192, 16384) == {"path": 2, "waves": 4, "chunks": 8, "grid": 8192}
+    assert plan(8, 8192, 16384) == {"path": 4, "waves": 4, "chunks": 8, "grid": 8192 + 512}
     assert plan(4, 2048, 7168, 2) == {"path": 3, "waves": 4, "chunks": 4, "grid": 256}
     assert plan(8, 128, 4096) == {"path": 2, "waves": 8, "chunks": 1, "grid": 128}
     assert plan(8, 64, 8192) == {"path": 2, "waves": 8, "chunks": 2, "grid": 64}
     assert plan(2, 16, 1024)["path"] == 2
     assert plan(4, 4096, 7168) == {"path": 2, "waves": 4, "chunks": 4, "grid": 4096}
+    assert plan(4, 4096, 7168, 2) == {"path": 4, "waves": 4, "chunks": 4, "grid": 4096 + 256}
     assert plan(2, 1024, 4096) == {"path": 2, "waves": 4, "chunks": 2, "grid": 1024}
     assert plan(8, 8192, 65536) == {"path": 2, "waves": 16, "chunks": 8, "grid": 8192}
 
@@ -175,6 +179,21 @@ def test_plan_held_rows_region():
     assert plan(4, 767, 7168, 2, 128)["path"] == 2 and plan(4, 768, 7168, 2, 128)["path"] == 3
 
 
+def test_plan_claim_region():
+    # rows claimed in start order: 4 wavefronts per row, and >= 16 rows per CU with >= 128
+    # KiB of traffic per row, or >= 8 rows per CU with >= 256 KiB per row (bf16 8 x 8192:
+    # 176 KiB per row; 1 x 16384: exactly 128 KiB; 8 x 16384: 368 KiB)
+    assert plan(8, 4095, 8192)["path"] == 2 and plan(8, 4096, 8192)["path"] == 4
+    assert plan(1, 4096, 16384)["path"] == 4 and plan(1, 4096, 16376)["path"] == 2
+    assert plan(8, 2047, 16384)["path"] == 2 and plan(8, 2048, 16384)["path"] == 4
+    assert plan(8, 8192, 4096)["path"] == 2            # 88 KiB per row
+    assert plan(5, 4096, 7168, 2) == {"path": 4, "waves": 4, "chunks": 4, "grid": 4096 + 256}
+    assert plan(8, 8192, 65536)["path"] == 2           # 16 wavefronts
+    assert plan(8, 64 * 1024, 16384)["grid"] == 64 * 1024 + 4096
+    # the thresholds scale with the CU count
+    assert plan(8, 1023, 16384, 0, 128)["path"] == 2 and plan(8, 1024, 16384, 0, 128)["path"] == 4
+
+
 def test_path_override_forces_and_rejects():
     try:
         arf.arf_set_path_override(1)
@@ -191,7 +210,13 @@ def test_path_override_forces_and_rejects():
             plan(8, 8, 16392)            # more than 8 chunks per lane
         arf.arf_set_path_override(3, 4, 4)
         assert plan(8, 100, 4096) == {"path": 3, "waves": 4, "chunks": 4, "grid": 100}
-        for bad in ((4, 0, 0), (0, 4, 0), (2, 3, 0), (2, 2, 0), (2, 4, 3), (1, 8, 0), (3, 8, 0)):
+        arf.arf_set_path_override(4)     # every row claimed, any size
+        assert plan(8, 100, 4096) == {"path": 4, "waves": 4, "chunks": 2, "grid": 164}
+        assert plan(8, 8192, 1024)["path"] == 4
+        arf.arf_set_path_override(4, 8, 0)
+        assert plan(8, 3, 16384) == {"path": 4, "waves": 8, "chunks": 4, "grid": 67}
+        for bad in ((5, 0, 0), (0, 4, 0), (2, 3, 0), (2, 2, 0), (2, 4, 3), (1, 8, 0), (3, 8, 0),
+                    (4, 2, 0), (4, 4, 3)):
             with pytest.raises(arf.ArfError):
                 arf.arf_set_path_override(*bad)
     finally:

@@ -183,11 +183,12 @@ def test_workload_parity_full(key):
     print(w.name, stats)
 
 
-@pytest.mark.parametrize("path", [0, 3])
+@pytest.mark.parametrize("path", [0, 2, 3])
 def test_workload_c4_full_size_every_row(path):
     # the largest workload at full size, in the launch configuration the benchmark times
-    # (path 0: the plan), and with the held-row kernel forced (eight batches of four rows
-    # per workgroup): every row against the oracle, 1024 rows at a time
+    # (path 0: the plan, rows claimed in start order), with rows by workgroup index (path
+    # 2), and with the held-row kernel forced (eight batches of four rows per workgroup):
+    # every row against the oracle, 1024 rows at a time
     w = workloads.WORKLOADS["c4"]
     say("workload %s full size, every row, path %d" % (w.name, path))
     p, r, g = workloads.generate(w, DEV)
@@ -260,8 +261,9 @@ XH = (8, 16, 64, 264, 1024, 2048, 4096, 7168, 8192, 16384)
 def test_cross_product_sweep_both_paths(pd, ad):
     # N x T x H over small token counts, per-token fp8 on every other case, each case on
     # the planned geometry, again with the other one-row path forced (one row per wavefront
-    # only where a wavefront covers the row), and with the held-row kernel forced; every
-    # fourth case in place
+    # only where a wavefront covers the row), with the held-row kernel forced, and with
+    # every row claimed from the stream's counter (calls of many sizes one after another on
+    # one stream: each must find the counter back at 0); every fourth case in place
     for n in XN:
         for t in XT:
             for h in XH:
@@ -272,8 +274,8 @@ def test_cross_product_sweep_both_paths(pd, ad):
                 auto = arf.arf_get_plan(n, t, h, {"bf16": 0, "f16": 1, "f32": 2}[pd])["path"]
                 other = 2 if auto == 1 else (1 if h <= 4096 else None)
                 in_place = (n + t + h // 8) % 4 == 0
-                for forced in (0, other, 3):
-                    if forced is None or (forced == 3 and auto == 3):
+                for forced in (0, other, 3, 4):
+                    if forced is None or forced == auto:
                         continue
                     say("cross n=%d t=%d h=%d %s/%s quant=%s path=%s in_place=%s"
                         % (n, t, h, pd, ad, quant, forced or "auto", in_place))
@@ -296,6 +298,9 @@ def _geometries(h):
                 out.append((2, wv, c))
         if 256 * c >= hc:
             out.append((3, 4, c))   # held rows: 4 wavefronts
+        for wv in (4, 8, 16):
+            if wv * 64 * c >= hc:
+                out.append((4, wv, c))   # one row per workgroup, every row claimed
     return out
 
 
@@ -449,9 +454,11 @@ def test_repeat_runs_are_bit_identical():
 
 
 
-def test_concurrent_calls_from_two_threads_on_two_streams():
-    # the library keeps no per-call state: two host threads enqueue calls with different
-    # shapes, types and modes on their own streams at the same time
+@pytest.mark.parametrize("path", [0, 4])
+def test_concurrent_calls_from_two_threads_on_two_streams(path):
+    # two host threads enqueue calls with different shapes, types and modes on their own
+    # streams at the same time; with path 4 every row is claimed, each stream from its own
+    # counter while the other stream's launches run
     import threading
 
     cases = [_case(8, 128, 4096, "bf16", "bf16", 601),
@@ -488,11 +495,15 @@ def test_concurrent_calls_from_two_threads_on_two_streams():
 
     threads = [threading.Thread(target=enqueue, args=(w, ins, outs, st))
                for w, ins, outs, _, st in work]
-    for th in threads:
-        th.start()
-    for th in threads:
-        th.join()
-    torch.cuda.synchronize()
+    try:
+        arf.arf_set_path_override(path)
+        for th in threads:
+            th.start()
+        for th in threads:
+            th.join()
+        torch.cuda.synchronize()
+    finally:
+        arf.arf_set_path_override(0)
     assert not errors, errors
     for w, _, outs, ref, _ in work:
         got = {}
@@ -590,7 +601,7 @@ def test_partial_accumulation_golden_on_gpu():
         assert torch.all(out.double() == float(vals[4])) and torch.all(sums.double() == float(vals[4]))
 
 
-@pytest.mark.parametrize("path", [0, 3])
+@pytest.mark.parametrize("path", [0, 3, 4])
 @pytest.mark.parametrize("begin,count", [(0, 7), (5, 11), (13, -1), (40, 1), (0, -1), (20, 0)])
 def test_row_ranges(begin, count, path):
     w = _case(8, 41, 4096, "bf16", "bf16", 600, quant="per_token")
@@ -787,13 +798,81 @@ def test_partials_above_4_gib():
     torch.cuda.empty_cache()
 
 
+# ---- rows claimed from a counter ----------------------------------------------------------
+
+def test_claimed_rows_on_more_streams_than_counters():
+    # 264 streams, more than the 256 counters of a device: each stream runs every-row-
+    # claimed calls of two sizes one after another; the streams that find no free counter
+    # take rows by workgroup index. Every output must equal the oracle's.
+    w = _case(4, 70, 1024, "bf16", "bf16", 611, quant="per_token")
+    w2 = _case(4, 33, 1024, "bf16", "bf16", 611, quant="per_token")
+    say("claimed rows on 264 streams")
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    ref = run_oracle(p, r, g, w.eps, "bf16", "bf16", quant="per_token")
+    ref2 = run_oracle(p[:, :33].contiguous(), r[:33].contiguous(), g, w.eps, "bf16", "bf16",
+                      quant="per_token")
+    t, h = w.tokens, w.hidden
+    pd33, rd33 = pd_[:, :33].contiguous(), rd[:33].contiguous()   # alive until the end
+    streams = [torch.cuda.Stream() for _ in range(264)]
+    outs = []
+    torch.cuda.synchronize()
+    try:
+        arf.arf_set_path_override(4)
+        for k, st in enumerate(streams):
+            o = {"residual_out": Out((t, h), torch.bfloat16), "norm_out": Out((t, h), torch.bfloat16),
+                 "quant_out": Out((t, h), torch.uint8), "scale_out": Out((t,), torch.float32)}
+            o2 = {"residual_out": Out((33, h), torch.bfloat16), "norm_out": Out((33, h), torch.bfloat16),
+                  "quant_out": Out((33, h), torch.uint8), "scale_out": Out((33,), torch.float32)}
+            torch.cuda.synchronize()
+            for oo, pp, rr in ((o, pd_, rd), (o2, pd33, rd33), (o, pd_, rd)):
+                arf.arf_reduce_add_rmsnorm_quant(
+                    pp, rr, gd, w.eps, oo["quant_out"].t, arf.ARF_QUANT_PER_TOKEN,
+                    scale_out=oo["scale_out"].t, residual_out=oo["residual_out"].t,
+                    norm_out=oo["norm_out"].t, stream=st)
+            outs.append((o, o2))
+        torch.cuda.synchronize()
+    finally:
+        arf.arf_set_path_override(0)
+    for k, (o, o2) in enumerate(outs):
+        for oo, rf, label in ((o, ref, "stream %d" % k), (o2, ref2, "stream %d (33 rows)" % k)):
+            got = {}
+            for name, x in oo.items():
+                assert x.canary_ok(), (label, name)
+                got[name] = x.t.cpu().numpy() if name in ("quant_out", "scale_out") else workloads.to_bits(x.t)
+            compare(got, rf, label)
+
+
+def test_claim_plan_fp32_partials_every_row():
+    # a shape the plan sends to claimed rows (4 fp32 shards of 4096 x 7168: 16 rows per
+    # compute unit, 154 KiB per row), every row against the oracle
+    w = _case(4, 4096, 7168, "f32", "bf16", 612)
+    plan = arf.arf_get_plan(4, 4096, 7168, 2)
+    assert plan["path"] == 4, plan
+    say("claim plan %s" % plan)
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    ref = run_oracle(p, r, g, w.eps, "f32", "bf16")
+    got = run_gpu(pd_, rd, gd, w.eps, "bf16")
+    compare(got, ref, "4 x 4096 x 7168 f32, claimed rows")
+
+
 # ---- HIP graph capture --------------------------------------------------------------------
 
-def test_graph_capture_and_replay():
+@pytest.mark.parametrize("path", [0, 4])
+def test_graph_capture_and_replay(path):
     # the fused call captured into a graph on a side stream, replayed with eager work
-    # (poisoning the outputs) in between; every replay must equal the eager result
+    # (poisoning the outputs) in between; every replay must equal the eager result. With
+    # path 4 the eager call claims its rows and the captured one takes them by workgroup
+    # index (a graph may be replayed on any stream): the same bits
     w = workloads.WORKLOADS["c1"]
-    say("graph capture / replay %s" % w.name)
+    say("graph capture / replay %s path %d" % (w.name, path))
+    arf.arf_set_path_override(path)
+    try:
+        _graph_capture_and_replay(w)
+    finally:
+        arf.arf_set_path_override(0)
+
+
+def _graph_capture_and_replay(w):
     (p, r, g), (pd_, rd, gd) = upload(w)
     t, h = w.tokens, w.hidden
     eager = run_gpu(pd_, rd, gd, w.eps, "bf16", quant="per_token")
@@ -983,10 +1062,11 @@ def _random_case(rng, k):
                 scale=float(rng.uniform(1e-3, 0.1)), seed=9000 + k)
 
 
-@pytest.mark.parametrize("path", [0, 3])
+@pytest.mark.parametrize("path", [0, 3, 4])
 def test_seeded_random_general_calls_match_the_oracle(path):
     # path 0: the plan; path 3: the held-row kernel forced on every call (one or several
-    # batches per workgroup, row ranges, in place, every quantised copy)
+    # batches per workgroup, row ranges, in place, every quantised copy); path 4: every row
+    # of every call claimed from the stream's counter
     try:
         arf.arf_set_path_override(path)
         _random_general_calls(path)
