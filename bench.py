@@ -272,6 +272,8 @@ def main():
         launch2 = percentiles_us(run2.distribution(steps2))
         mix2 = None if args.no_copy_probe else mix_probe(w2, run2, stream)
         best2 = None if args.no_copy_probe else best_mix_probe(w2, run2, stream, mix2)
+        dir2 = None if args.no_copy_probe else direction_probes(
+            w2, [s_[0] for s_ in run2.sets], stream)
         del run2
         torch.cuda.empty_cache()
         secondary = {"workload": w2.name, "buffer_sets": sets, "steps": steps2,
@@ -288,7 +290,10 @@ def main():
                                               round(B2 / (kms2 * 1e-3) / 1e9 / mix2, 4),
                      "best_mix": best2,
                      "frac_of_best_mix": None if best2 is None else
-                                         round(B2 / (kms2 * 1e-3) / 1e9 / best2["GBs"], 4)}
+                                         round(B2 / (kms2 * 1e-3) / 1e9 / best2["GBs"], 4),
+                     "direction_probes": dir2,
+                     "frac_of_serial": None if dir2 is None else
+                                       round(B2 / (kms2 * 1e-3) / 1e9 / dir2["serial_GBs"], 4)}
 
     cpu = None
     parity = None
@@ -335,6 +340,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "hbm_probes": probes,
+        "frac_of_serial": None if probes is None else round(achieved / probes["serial_GBs"], 4),
         "frac_of_best_mix": None if probes is None else round(achieved / probes["best_mix_GBs"], 4),
         "frac_of_row_mix_probe": None if probes is None else round(achieved / probes["row_mix_GBs"], 4),
         "secondary": secondary,
@@ -409,23 +415,78 @@ def best_mix_probe(w, run, stream, row_mix, reps=10):
     return best
 
 
+def _alg_split(w):
+    """The workload's algorithmic bytes read and written per launch."""
+    n, t, h = w.n_shards, w.tokens, w.hidden
+    B = w.algorithmic_bytes()
+    alg_read = n * t * h * w.sp + t * h * w.sa + h * w.sa + (4 if w.quant == "per_tensor" else 0)
+    return alg_read, B - alg_read
+
+
+UNIT_COUNTS = (256, 512, 1024, 2048, 4096)
+
+
+def direction_probes(w, srcs, stream, reps=10):
+    """Best read-only and write-only rates (GB/s) with no arithmetic, over several unit
+    counts (256..4096 workgroups, and one per 16 KiB): reading each source buffer (the
+    partials) in turn, and writing the workload's algorithmic write bytes to one buffer per
+    source in turn, so that rotating sets larger than the 256 MB Infinity Cache are not
+    served from it. serial_us is the time to read the workload's algorithmic read bytes at
+    the read rate and then write its write bytes at the write rate: the pass with no
+    overlap of reads and writes on the bus."""
+    import torch
+
+    import shard_reduce_residual_amd as arf
+
+    alg_read, alg_write = _alg_split(w)
+    read_b = srcs[0].numel() * srcs[0].element_size()
+    write_b = (alg_write // 16) * 16
+    dsts = [torch.empty(write_b, dtype=torch.uint8, device=srcs[0].device) for _ in srcs]
+
+    def best(call):
+        top = (0.0, 0)
+        for units in UNIT_COUNTS + (0,):
+            k = [0]
+
+            def one():
+                i = k[0] % len(srcs)
+                k[0] += 1
+                call(i, units)
+
+            ms = _events_ms(one, stream, reps, 3)
+            top = max(top, (1.0 / ms, units))
+        return 1.0 / top[0], top[1]
+
+    ms_r, u_r = best(lambda i, u: arf.arf_stream_mix(None, 0, srcs[i], read_b, units=u,
+                                                     stream=stream))
+    ms_w, u_w = best(lambda i, u: arf.arf_stream_mix(dsts[i], write_b, None, 0, units=u,
+                                                     stream=stream))
+    del dsts
+    read_gbs = read_b / (ms_r * 1e-3) / 1e9
+    write_gbs = write_b / (ms_w * 1e-3) / 1e9
+    serial_us = (alg_read / read_gbs + alg_write / write_gbs) / 1e3
+    return {"read_GBs": round(read_gbs, 1), "read_units": u_r or "per 16 KiB",
+            "write_GBs": round(write_gbs, 1), "write_units": u_w or "per 16 KiB",
+            "write_bytes": write_b, "serial_us": round(serial_us, 2),
+            "serial_GBs": round(w.algorithmic_bytes() / (serial_us * 1e-6) / 1e9, 1)}
+
+
 def hbm_probes(w, partials, stream, reps=10):
-    """Streaming kernels with no arithmetic (GB/s): read only, write only, a copy, and the
-    workload's own read/write mix -- reading the partials buffer and writing a buffer in
-    the workload's write:read ratio -- once as one unit per row (reads, then writes, per
-    unit, as the fused kernel does: row_mix) and once as the best over 1/32 .. 1 units per
-    row (best_mix, the fastest pattern measured for this byte mix)."""
+    """Streaming kernels with no arithmetic (GB/s): the best read-only and write-only rates
+    and the serial pass they imply (direction_probes), a 1 GiB copy, and the workload's
+    own read/write mix -- reading the partials buffer and writing a buffer in the
+    workload's write:read ratio -- once as one unit per row (reads, then writes, per unit:
+    row_mix) and once as the best over 1/32 .. 1 units per row (best_mix)."""
     import torch
 
     import shard_reduce_residual_amd as arf
 
     dev = partials.device
     read_b = partials.numel() * partials.element_size()
-    B = w.algorithmic_bytes()
-    n, t, h = w.n_shards, w.tokens, w.hidden
-    alg_read = n * t * h * w.sp + t * h * w.sa + h * w.sa + (4 if w.quant == "per_tensor" else 0)
-    alg_write = B - alg_read
+    t = w.tokens
+    alg_read, alg_write = _alg_split(w)
     mix_write = (int(read_b * alg_write / alg_read) // 16) * 16
+    out = direction_probes(w, [partials], stream, reps)
     one_gib = 1 << 30
     dst = torch.empty(max(mix_write, one_gib), dtype=torch.uint8, device=dev)
     flat = partials.view(torch.uint8).view(-1)
@@ -446,11 +507,6 @@ def hbm_probes(w, partials, stream, reps=10):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps * 1e-3
 
-    out = {}
-    t_r = timed(lambda: arf.arf_stream_mix(None, 0, partials, read_b, stream=stream))
-    out["read_GBs"] = round(read_b / t_r / 1e9, 1)
-    t_w = timed(lambda: arf.arf_stream_mix(dst, one_gib, None, 0, stream=stream))
-    out["write_GBs"] = round(one_gib / t_w / 1e9, 1)
     t_c = timed(lambda: arf.arf_stream_copy(dst, src2, one_gib, stream=stream))
     out["copy_GBs"] = round(2 * one_gib / t_c / 1e9, 1)
     t_m = timed(lambda: arf.arf_stream_mix(dst, mix_write, partials, read_b, units=t,

@@ -40,6 +40,12 @@ def test_bench_prints_one_contract_line():
     hp = d["hbm_probes"]
     assert hp["best_mix_GBs"] >= hp["row_mix_GBs"] > 0 and hp["best_mix_units"] >= 1
     assert abs(d["frac_of_best_mix"] - rl["achieved"] / hp["best_mix_GBs"]) < 1e-3
+    # the best single-direction rates and the serial pass they imply
+    assert hp["read_GBs"] > 0 and hp["write_GBs"] > 0 and hp["serial_us"] > 0
+    serial_gbs = d["config"]["algorithmic_bytes"] / (hp["serial_us"] * 1e-6) / 1e9
+    assert abs(serial_gbs / hp["serial_GBs"] - 1) < 1e-3
+    assert abs(d["frac_of_serial"] - rl["achieved"] / hp["serial_GBs"]) < 1e-3
+    assert d["secondary"]["direction_probes"]["serial_GBs"] > 0
     assert d["secondary"]["workload"] == "c2_n8_t64_h8192_bf16_fp8tensor"
     assert d["secondary"]["best_mix"]["GBs"] > 0
     for key in ("c0_n2_t16_h1024_bf16", "c1_n8_t128_h4096_bf16",
