@@ -591,7 +591,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
 // LDS (size set by the host): K rows of hidden*2 bytes, then K*WAVES fp64 partial sums of
 // squares and K*WAVES fp32 maxima. Only hidden/8 <= C * WAVES * 64 is supported (the host
 // checks).
-template <class PT, class AT, int N, int C, int WAVES>
+template <class PT, class AT, int N, int C, int WAVES, bool QUANT>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fused_held_rows(Params p) {
     constexpr int PW = PartTraits<PT>::kPieces;
@@ -616,7 +616,12 @@ void fused_held_rows(Params p) {
     u32x4 gv[C];
 #pragma unroll
     for (int j = 0; j < C; ++j) gv[j] = LW::template load_act<kAuxDefault>(g_in, j, gl);
-    const float scale_tensor = p.quant_mode == kQuantTensor ? p.scale_in[0] : 0.0f;
+    // QUANT = false: the instantiation for calls without a quantised copy. Without the
+    // quantisation paths the kernel needs fewer scalar registers: the general form spills
+    // 74 of them into vector-register lanes, reloaded inside the row loop (4 fp32 shards of
+    // 2048 x 7168: 53.5 -> 51.4 us).
+    const int32_t qmode = QUANT ? p.quant_mode : (int32_t)kQuantNone;
+    const float scale_tensor = qmode == kQuantTensor ? p.scale_in[0] : 0.0f;
 
     auto hold_store = [&](char* row, int j, u32x4 v) {   // chunk j of the read layout
         if constexpr (SPLIT) {
@@ -656,7 +661,10 @@ void fused_held_rows(Params p) {
     int64_t seq = 0;               // rows taken so far: the current row is T(seq)
     int64_t cur = ticket(0), nxt = ticket(1);
 
-    u32x4 pf[D - 1][C][PW];   // the first D-1 shards of the next row
+    // Shard segments of the current row. Slots [0, D-1) arrive loaded ahead: the next row's
+    // first D-1 shards are issued into them once the current row has consumed them, so no
+    // copy between registers (which would wait for the loads in flight) is needed.
+    u32x4 sb[N][C][PW];
     while (cur < rows) {
         // ---- read half: up to K rows in, r held in LDS
         {
@@ -668,7 +676,7 @@ void fused_held_rows(Params p) {
                 for (int j = 0; j < C; ++j)
 #pragma unroll
                     for (int w = 0; w < PW; ++w)
-                        pf[d][j][w] = __builtin_amdgcn_raw_buffer_load_b128(rs, L::part(j, w, gl), 0, kAuxStream);
+                        sb[d][j][w] = __builtin_amdgcn_raw_buffer_load_b128(rs, L::part(j, w, gl), 0, kAuxStream);
             }
         }
         int kn = 0;
@@ -681,21 +689,15 @@ void fused_held_rows(Params p) {
 #pragma unroll
             for (int r = 0; r < N; ++r) part[r] = shard_rsrc(row, r, true);
             const auto r_in = make_rsrc((const char*)p.residual_in + row * (int64_t)act_row, act_row);
-            u32x4 sb[N][C][PW];
             u32x4 rv[C];
-#pragma unroll
-            for (int d = 0; d < D - 1; ++d)
-#pragma unroll
-                for (int j = 0; j < C; ++j)
-#pragma unroll
-                    for (int w = 0; w < PW; ++w) sb[d][j][w] = pf[d][j][w];
             float acc[C][8];
             double ss = 0.0;
             char* hrow = s_dyn + (size_t)k * act_row;
 #pragma unroll
             for (int s = 0; s <= N; ++s) {
                 const int t = s + D - 1;   // segment issued now: shard t, the residual (t == N),
-                if (t < N) {               // or shard t - N - 1 of the next row
+                if (t < N) {               // or shard t - N - 1 of the next row, into its
+                                           // slot (consumed at step t - N - 1 < s)
 #pragma unroll
                     for (int j = 0; j < C; ++j)
 #pragma unroll
@@ -710,7 +712,7 @@ void fused_held_rows(Params p) {
                     for (int j = 0; j < C; ++j)
 #pragma unroll
                         for (int w = 0; w < PW; ++w)
-                            pf[t - N - 1][j][w] = __builtin_amdgcn_raw_buffer_load_b128(rs, L::part(j, w, gl), 0, kAuxStream);
+                            sb[t - N - 1][j][w] = __builtin_amdgcn_raw_buffer_load_b128(rs, L::part(j, w, gl), 0, kAuxStream);
                 }
                 if (s < N) {
 #pragma unroll
@@ -759,7 +761,7 @@ void fused_held_rows(Params p) {
         __syncthreads();
 
         // ---- per-token maxima of the cast outputs (needed before the first code is written)
-        if (p.quant_mode == kQuantToken) {
+        if (qmode == kQuantToken) {
             for (int k = 0; k < kn; ++k) {
                 const float inv = row_inv(k);
                 const char* hrow = s_dyn + (size_t)k * act_row;
@@ -793,14 +795,14 @@ void fused_held_rows(Params p) {
             const char* hrow = s_dyn + (size_t)k * act_row;
             const float inv = row_inv(k);
             float inv_scale = 0.0f;
-            if (p.quant_mode == kQuantToken) {
+            if (qmode == kQuantToken) {
                 float amax = 0.0f;
 #pragma unroll
                 for (int w = 0; w < WAVES; ++w) amax = fmaxf(amax, s_mx[k * WAVES + w]);
                 const float scale = amax / 448.0f;
                 if (gl == 0) static_cast<float*>(p.scale_out)[row] = scale;
                 inv_scale = scale > 0.0f ? 1.0f / scale : 0.0f;
-            } else if (p.quant_mode == kQuantTensor) {
+            } else if (qmode == kQuantTensor) {
                 inv_scale = scale_tensor > 0.0f ? 1.0f / scale_tensor : 0.0f;
             }
             const auto q_out = make_rsrc(p.quant_out + row * (int64_t)H, p.quant_out ? H : 0u);
@@ -820,10 +822,10 @@ void fused_held_rows(Params p) {
                 }
                 const u32x4 yr = pack8(AT{}, y);
                 LW::store_act(yr, y_out, j, gl);
-                if (p.quant_mode == kQuantNone) continue;
+                if (qmode == kQuantNone) continue;
                 float yc[8];
                 unpack8(AT{}, yr, yc);
-                if (p.quant_mode == kQuantMx) {
+                if (qmode == kQuantMx) {
                     LW::store_mx(yc, q_mx, s_mxo, j, gl);
                 } else {
                     u32x2 q;
@@ -853,12 +855,12 @@ hipError_t launch_fused(const Params& p, uint32_t grid, uint32_t lds, hipStream_
 typedef hipError_t (*launch_fn)(const Params&, uint32_t, uint32_t, hipStream_t);
 
 // Held-row kernel launcher: `lds` bytes of dynamic LDS per workgroup.
-template <class PT, class AT, int N, int C, int WAVES>
+template <class PT, class AT, int N, int C, int WAVES, bool QUANT>
 hipError_t launch_held(const Params& p, uint32_t grid, uint32_t lds, hipStream_t stream) {
     Params arg = p;
     void* args[] = {&arg};
     return hipLaunchKernel(
-        reinterpret_cast<const void*>(&fused_held_rows<PT, AT, N, C, WAVES>),
+        reinterpret_cast<const void*>(&fused_held_rows<PT, AT, N, C, WAVES, QUANT>),
         dim3(grid), dim3(WAVES * 64), args, lds, stream);
 }
 

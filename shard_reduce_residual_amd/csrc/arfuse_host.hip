@@ -262,12 +262,12 @@ arf_status make_plan(int64_t tokens, int32_t hidden, int n, int quant, int64_t r
     return ARF_OK;
 }
 
-held_launch_fn lookup_held(int pdt, int adt, int n, int c) {
-#define ARF_BY_RANGE(PD, AD)                                          \
-    if (n <= 4) return arf::held_##PD##_##AD##_n01_04(n, c);          \
-    if (n <= 8) return arf::held_##PD##_##AD##_n05_08(n, c);          \
-    if (n <= 12) return arf::held_##PD##_##AD##_n09_12(n, c);         \
-    return arf::held_##PD##_##AD##_n13_16(n, c);
+held_launch_fn lookup_held(int pdt, int adt, int n, int c, bool quant) {
+#define ARF_BY_RANGE(PD, AD)                                                 \
+    if (n <= 4) return arf::held_##PD##_##AD##_n01_04(n, c, quant);          \
+    if (n <= 8) return arf::held_##PD##_##AD##_n05_08(n, c, quant);          \
+    if (n <= 12) return arf::held_##PD##_##AD##_n09_12(n, c, quant);         \
+    return arf::held_##PD##_##AD##_n13_16(n, c, quant);
     if (adt == ARF_BF16) {
         if (pdt == ARF_F32) { ARF_BY_RANGE(f32, bf16) }
         ARF_BY_RANGE(bf16, bf16)
@@ -443,7 +443,7 @@ arf_status run(Call c, void* stream) {
     }
     launch_fn fn = nullptr;
     held_launch_fn hfn = nullptr;
-    if (pl.path == 3) hfn = lookup_held(c.pdt, c.adt, c.n, pl.chunks);
+    if (pl.path == 3) hfn = lookup_held(c.pdt, c.adt, c.n, pl.chunks, c.quant != arf::kQuantNone);
     else fn = lookup(c.pdt, c.adt, c.n, pl);
     if (!fn && !hfn) return ARF_ERR_VALUE;
     arf::Params p;

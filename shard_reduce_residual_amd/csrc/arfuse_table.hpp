@@ -65,23 +65,33 @@ launch_fn pick_shards(int n, bool row_per_wave, int waves, int c) {
 }
 
 // Held-row kernel: 4 wavefronts (one per SIMD, so each may use the whole register file),
-// chunks per lane in {1, 2, 4, 8}: rows of up to 16384 elements.
-template <class PT, class AT, int N>
-held_launch_fn pick_held(int c) {
+// chunks per lane in {1, 2, 4, 8}: rows of up to 16384 elements. Every shard count has the
+// general form (any quantised copy); the shard counts the plan sends to held rows (1..4)
+// also have the form without a quantised copy, which those calls take.
+template <class PT, class AT, int N, bool QUANT>
+held_launch_fn pick_held_c(int c) {
     switch (c) {
-        case 1: return &launch_held<PT, AT, N, 1, 4>;
-        case 2: return &launch_held<PT, AT, N, 2, 4>;
-        case 4: return &launch_held<PT, AT, N, 4, 4>;
-        case 8: return &launch_held<PT, AT, N, 8, 4>;
+        case 1: return &launch_held<PT, AT, N, 1, 4, QUANT>;
+        case 2: return &launch_held<PT, AT, N, 2, 4, QUANT>;
+        case 4: return &launch_held<PT, AT, N, 4, 4, QUANT>;
+        case 8: return &launch_held<PT, AT, N, 8, 4, QUANT>;
         default: return nullptr;
     }
 }
 
+template <class PT, class AT, int N>
+held_launch_fn pick_held(int c, bool quant) {
+    if constexpr (N <= 4) {
+        if (!quant) return pick_held_c<PT, AT, N, false>(c);
+    }
+    return pick_held_c<PT, AT, N, true>(c);
+}
+
 template <class PT, class AT, int NLO, int NHI>
-held_launch_fn pick_held_shards(int n, int c) {
+held_launch_fn pick_held_shards(int n, int c, bool quant) {
     if constexpr (NLO <= NHI) {
-        if (n == NLO) return pick_held<PT, AT, NLO>(c);
-        return pick_held_shards<PT, AT, NLO + 1, NHI>(n, c);
+        if (n == NLO) return pick_held<PT, AT, NLO>(c, quant);
+        return pick_held_shards<PT, AT, NLO + 1, NHI>(n, c, quant);
     } else {
         return nullptr;
     }
@@ -93,10 +103,10 @@ held_launch_fn pick_held_shards(int n, int c) {
     launch_fn lookup_##PD##_##AD##_n05_08(int n, bool rpw, int waves, int c);    \
     launch_fn lookup_##PD##_##AD##_n09_12(int n, bool rpw, int waves, int c);    \
     launch_fn lookup_##PD##_##AD##_n13_16(int n, bool rpw, int waves, int c);    \
-    held_launch_fn held_##PD##_##AD##_n01_04(int n, int c);                      \
-    held_launch_fn held_##PD##_##AD##_n05_08(int n, int c);                      \
-    held_launch_fn held_##PD##_##AD##_n09_12(int n, int c);                      \
-    held_launch_fn held_##PD##_##AD##_n13_16(int n, int c);
+    held_launch_fn held_##PD##_##AD##_n01_04(int n, int c, bool quant);                      \
+    held_launch_fn held_##PD##_##AD##_n05_08(int n, int c, bool quant);                      \
+    held_launch_fn held_##PD##_##AD##_n09_12(int n, int c, bool quant);                      \
+    held_launch_fn held_##PD##_##AD##_n13_16(int n, int c, bool quant);
 ARF_DECLARE_LOOKUPS(bf16, bf16)
 ARF_DECLARE_LOOKUPS(f16, f16)
 ARF_DECLARE_LOOKUPS(f32, bf16)

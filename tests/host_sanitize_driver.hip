@@ -13,7 +13,7 @@
 namespace arf {
 #define ARF_STUB(PD, AD, R)                                                         \
     launch_fn lookup_##PD##_##AD##_##R(int, bool, int, int) { return nullptr; }     \
-    held_launch_fn held_##PD##_##AD##_##R(int, int) { return nullptr; }
+    held_launch_fn held_##PD##_##AD##_##R(int, int, bool) { return nullptr; }
 #define ARF_STUBS(PD, AD) \
     ARF_STUB(PD, AD, n01_04) ARF_STUB(PD, AD, n05_08) ARF_STUB(PD, AD, n09_12) ARF_STUB(PD, AD, n13_16)
 ARF_STUBS(bf16, bf16)
