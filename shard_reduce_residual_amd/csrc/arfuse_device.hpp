@@ -596,7 +596,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1
 void fused_held_rows(Params p) {
     constexpr int PW = PartTraits<PT>::kPieces;
     constexpr int G = WAVES * 64;              // lanes per row
-    constexpr int D = N + 1 < 3 ? N + 1 : 3;   // segments in flight (D - 1 <= N)
+    // segments in flight (D - 1 <= N): one ahead for fp32 partials, two for 16-bit ones (a
+    // sweep of 9 held-region shapes: one ahead 1.6-4% faster with fp32 partials, up to 10%
+    // slower with 16-bit ones)
+    constexpr int DS = PW == 2 ? 2 : 3;
+    constexpr int D = N + 1 < DS ? N + 1 : DS;
     constexpr bool SPLIT = PW == 2;
     using L = Layout<SPLIT, G>;
     using LW = Layout<false, G>;
@@ -641,6 +645,14 @@ void fused_held_rows(Params p) {
         const uint32_t c = (uint32_t)(j * G + gl);
         if (c < H / 8u) v = *reinterpret_cast<const u32x4*>(row + c * 16u);
         return v;
+    };
+    // The same without the zero fill: a lane past the row's end reads chunk 0 instead. For
+    // the write half only, whose stores past the row's end the range check drops (an MXFP4
+    // block never straddles the end, since hidden % 32 == 0): with no branch per chunk the
+    // reads of a row issue together.
+    auto hold_load_any = [&](const char* row, int j) {
+        const uint32_t c = (uint32_t)(j * G + gl);
+        return *reinterpret_cast<const u32x4*>(row + (c < H / 8u ? c : 0u) * 16u);
     };
     auto shard_rsrc = [&](int64_t row, int r, bool valid) {
         return make_rsrc((const char*)p.partials + ((int64_t)r * p.tokens + row) * (int64_t)part_row,
@@ -760,10 +772,21 @@ void fused_held_rows(Params p) {
         }
         __syncthreads();
 
+        // inv of held row k is formed by lane k of every wavefront, in parallel: one chain of
+        // fp64 divide and square root per wavefront instead of one per row, which with one
+        // wavefront per SIMD nothing else would hide. Rows beyond the 64th (small hidden
+        // sizes only) form theirs in turn. Same operations, so the same bits.
+        const float inv_lane = lane < kn ? row_inv(lane) : 0.0f;
+        auto inv_of = [&](int k) {
+            return k < 64 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                          __builtin_bit_cast(int, inv_lane), k))
+                          : row_inv(k);
+        };
+
         // ---- per-token maxima of the cast outputs (needed before the first code is written)
         if (qmode == kQuantToken) {
             for (int k = 0; k < kn; ++k) {
-                const float inv = row_inv(k);
+                const float inv = inv_of(k);
                 const char* hrow = s_dyn + (size_t)k * act_row;
                 float amax = 0.0f;
 #pragma unroll
@@ -793,7 +816,7 @@ void fused_held_rows(Params p) {
             const auto r_out = make_rsrc((char*)p.residual_out + act_off, p.residual_out ? act_row : 0u);
             const auto y_out = make_rsrc((char*)p.norm_out + act_off, p.norm_out ? act_row : 0u);
             const char* hrow = s_dyn + (size_t)k * act_row;
-            const float inv = row_inv(k);
+            const float inv = inv_of(k);
             float inv_scale = 0.0f;
             if (qmode == kQuantToken) {
                 float amax = 0.0f;
@@ -808,9 +831,12 @@ void fused_held_rows(Params p) {
             const auto q_out = make_rsrc(p.quant_out + row * (int64_t)H, p.quant_out ? H : 0u);
             const auto q_mx = make_rsrc(p.quant_out + row * (int64_t)(H / 2), p.quant_out ? H / 2 : 0u);
             const auto s_mxo = make_rsrc((uint8_t*)p.scale_out + row * (int64_t)(H / 32), p.scale_out ? H / 32 : 0u);
+            u32x4 rrs[C];
+#pragma unroll
+            for (int j = 0; j < C; ++j) rrs[j] = hold_load_any(hrow, j);
 #pragma unroll
             for (int j = 0; j < C; ++j) {
-                const u32x4 rr = hold_load(hrow, j);
+                const u32x4 rr = rrs[j];
                 LW::store_act(rr, r_out, j, gl);
                 float x[8], g[8], y[8];
                 unpack8(AT{}, rr, x);
