@@ -26,7 +26,9 @@
  *     never synchronises. Its only state is a per-device compute-unit count, the test-only
  *     override below, and the row-claim counters of large launches: a file-scope device
  *     array of 256 counters (64 KiB per device, no allocation), one per stream on first use
- *     and for the life of the process. A launch with claimed rows leaves its counter at 0.
+ *     and for the life of the process (a new stream that gets a destroyed stream's handle
+ *     gets its counter too: hipStreamDestroy completes the stream's pending work first on
+ *     ROCm). A launch with claimed rows leaves its counter at 0.
  *     Calls on one stream run one after another and share its counter; calls on different
  *     streams never share one. A call enqueued under stream capture, on the per-thread
  *     default stream, on a stream of another device, or once every counter belongs to

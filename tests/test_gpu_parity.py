@@ -10,6 +10,7 @@ Tolerances (fixed here, per output):
 Every element must pass. Output buffers are poisoned (0xFF) and followed by canary
 bytes, so an element that is never written, or a write past the end, fails.
 """
+import ctypes
 import numpy as np
 import pytest
 import torch
@@ -840,6 +841,48 @@ def test_claimed_rows_on_more_streams_than_counters():
                 assert x.canary_ok(), (label, name)
                 got[name] = x.t.cpu().numpy() if name in ("quant_out", "scale_out") else workloads.to_bits(x.t)
             compare(got, rf, label)
+
+
+def test_claimed_rows_on_recreated_streams():
+    # HIP gives a new stream the handle of one just destroyed, and with it that handle's
+    # counter. Six streams are created through the HIP runtime in turn; each runs two
+    # every-row-claimed calls and is destroyed right after them, with the last call
+    # possibly still pending. Every output must equal the oracle's.
+    hip = ctypes.CDLL("libamdhip64.so.7")   # the runtime torch has loaded (same soname)
+    hip.hipStreamCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    w = _case(4, 70, 1024, "bf16", "bf16", 613, quant="per_token")
+    say("claimed rows on 6 streams created and destroyed in turn")
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    ref = run_oracle(p, r, g, w.eps, "bf16", "bf16", quant="per_token")
+    t, h = w.tokens, w.hidden
+    outs, handles = [], []
+    for k in range(6):
+        o = {"residual_out": Out((t, h), torch.bfloat16), "norm_out": Out((t, h), torch.bfloat16),
+             "quant_out": Out((t, h), torch.uint8), "scale_out": Out((t,), torch.float32)}
+        torch.cuda.synchronize()   # the outputs' poison is written before the raw stream runs
+        s = ctypes.c_void_p()
+        assert hip.hipStreamCreate(ctypes.byref(s)) == 0
+        handles.append(s.value)
+        try:
+            arf.arf_set_path_override(4)
+            for _ in range(2):
+                arf.arf_reduce_add_rmsnorm_quant(
+                    pd_, rd, gd, w.eps, o["quant_out"].t, arf.ARF_QUANT_PER_TOKEN,
+                    scale_out=o["scale_out"].t, residual_out=o["residual_out"].t,
+                    norm_out=o["norm_out"].t, stream=s.value)
+        finally:
+            arf.arf_set_path_override(0)
+            assert hip.hipStreamDestroy(s) == 0
+        outs.append(o)
+    torch.cuda.synchronize()
+    say("stream handles: %d distinct of 6" % len(set(handles)))
+    for k, o in enumerate(outs):
+        got = {}
+        for name, x in o.items():
+            assert x.canary_ok(), (k, name)
+            got[name] = x.t.cpu().numpy() if name in ("quant_out", "scale_out") else workloads.to_bits(x.t)
+        compare(got, ref, "recreated stream %d" % k)
 
 
 def test_claim_plan_fp32_partials_every_row():
