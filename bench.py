@@ -158,7 +158,56 @@ def parse():
                              "copy"],
                     help="launch only this variant of the workload (warmup + steps times) "
                          "and print its timing, for profiler runs; no contract line")
+    ap.add_argument("--survey", action="store_true",
+                    help="time the planned path on a grid of shapes against the serial "
+                         "read-then-write probe for the same bytes; one JSON line per "
+                         "shape, no contract line")
     return ap.parse_args()
+
+
+# Shapes of the survey: (shards, tokens, hidden, partial type, quantised copy). Shapes
+# whose partials exceed 2 GiB are left out.
+SURVEY_SHAPES = (
+    [(n, t, h, "bf16", None) for n in (2, 4, 8, 16) for h in (2048, 4096, 8192, 16384)
+     for t in (1024, 4096, 16384)]
+    + [(4, t, h, "f32", None) for h in (4096, 7168, 8192) for t in (2048, 8192)]
+    + [(8, 4096, 8192, "bf16", "per_token"), (8, 8192, 16384, "bf16", "per_token"),
+       (8, 4096, 4096, "bf16", "per_token"), (4, 16384, 4096, "bf16", "per_token")])
+
+
+def survey(args, dev, stream):
+    """The plan on every shape of SURVEY_SHAPES (bf16 activations, synthetic inputs of
+    c4's distribution): kernel time from events over ``steps`` launches rotating input
+    sets of at least 1.5 GB, and the serial pass of direction_probes for the same bytes."""
+    import dataclasses
+
+    import torch
+
+    import shard_reduce_residual_amd as arf
+    import workloads
+
+    base = workloads.WORKLOADS["c4"]
+    for n, t, h, pdt, quant in SURVEY_SHAPES:
+        sp = 4 if pdt == "f32" else 2
+        if n * t * h * sp > 2 ** 31:
+            continue
+        w = dataclasses.replace(base, name="survey", n_shards=n, tokens=t, hidden=h,
+                                partial_dtype=pdt, quant=quant)
+        B = w.algorithmic_bytes()
+        run = Runner(w, dev, stream, sets=max(1, min(6, -(-1_500_000_000 // B))))
+        plan = arf.arf_get_plan(n, t, h, arf.ARF_F32 if pdt == "f32" else arf.ARF_BF16)
+        _, kms = run.measure(args.steps, args.warmup)
+        d = direction_probes(w, [s[0] for s in run.sets], stream, reps=8)
+        gbs = B / (kms * 1e-3) / 1e9
+        print(json.dumps({"shards": n, "tokens": t, "hidden": h, "partials": pdt,
+                          "quant": quant, "plan": plan, "kernel_us": round(kms * 1e3, 2),
+                          "GBs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                          "serial_us": d["serial_us"],
+                          "frac_of_serial": round(d["serial_us"] / (kms * 1e3), 4)}),
+              flush=True)
+        del run
+        torch.cuda.empty_cache()
+    return 0
 
 
 def profile_variant(args, w, run, stream):
@@ -246,6 +295,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream(device=dev)
+    if args.survey:
+        return survey(args, dev, stream)
     t, h = w.tokens, w.hidden
     B = w.algorithmic_bytes()
     # workloads smaller than 1.5 GB rotate input/output sets so that the 256 MB Infinity
@@ -258,6 +309,7 @@ def main():
     achieved = B / (kernel_ms * 1e-3) / 1e9
     traffic = read_traffic(w.name)
     launch_us = percentiles_us(run.distribution(max(args.steps, 20)))
+    sus = sustained(run, kernel_ms, B)
     p, r, g, rout, nout, q, sc_out, sc_in = run.sets[0]
 
     secondary = None
@@ -270,6 +322,7 @@ def main():
         steps2 = max(args.steps, 200)
         ms2, kms2 = run2.measure(steps2, max(args.warmup, 10))
         launch2 = percentiles_us(run2.distribution(steps2))
+        sus2 = sustained(run2, kms2, B2)
         mix2 = None if args.no_copy_probe else mix_probe(w2, run2, stream)
         best2 = None if args.no_copy_probe else best_mix_probe(w2, run2, stream, mix2)
         dir2 = None if args.no_copy_probe else direction_probes(
@@ -278,7 +331,7 @@ def main():
         torch.cuda.empty_cache()
         secondary = {"workload": w2.name, "buffer_sets": sets, "steps": steps2,
                      "ms_per_step": round(ms2, 5), "kernel_ms": round(kms2, 5),
-                     "launch_us": launch2,
+                     "launch_us": launch2, "sustained": sus2,
                      "achieved": round(B2 / (kms2 * 1e-3) / 1e9, 2), "unit": "GB/s",
                      "frac": round(B2 / (kms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "tokens_per_s": round(w2.tokens / (kms2 * 1e-3), 1),
@@ -339,6 +392,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
+        "sustained": sus,
         "hbm_probes": probes,
         "frac_of_serial": None if probes is None else round(achieved / probes["serial_GBs"], 4),
         "frac_of_best_mix": None if probes is None else round(achieved / probes["best_mix_GBs"], 4),
@@ -351,6 +405,18 @@ def main():
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def sustained(run, kernel_ms, nbytes, seconds=1.0):
+    """The same launches back to back for about ``seconds`` right after the timed region:
+    the kernel's average duration once the GPU has been busy for a while. The timed steps
+    follow a few seconds of start-up in which the GPU is mostly idle, and an MI355X that
+    has just been idle runs these launches slightly faster (c4: about 482 against 484 us)."""
+    n = max(20, min(20000, int(seconds / (kernel_ms * 1e-3))))
+    _, ms = run.measure(n, 0)
+    return {"launches": n, "kernel_ms": round(ms, 5),
+            "achieved": round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def mix_probe(w, run, stream, reps=20):

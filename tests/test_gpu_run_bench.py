@@ -46,6 +46,10 @@ def test_bench_prints_one_contract_line():
     assert abs(serial_gbs / hp["serial_GBs"] - 1) < 1e-3
     assert abs(d["frac_of_serial"] - rl["achieved"] / hp["serial_GBs"]) < 1e-3
     assert d["secondary"]["direction_probes"]["serial_GBs"] > 0
+    # the same launches back to back for about a second after the timed region
+    for sus in (d["sustained"], d["secondary"]["sustained"]):
+        assert sus["launches"] >= 20 and sus["kernel_ms"] > 0
+        assert abs(sus["frac"] - sus["achieved"] / rl["peak"]) < 1e-3
     assert d["secondary"]["workload"] == "c2_n8_t64_h8192_bf16_fp8tensor"
     assert d["secondary"]["best_mix"]["GBs"] > 0
     for key in ("c0_n2_t16_h1024_bf16", "c1_n8_t128_h4096_bf16",
