@@ -25,15 +25,15 @@
  *   - Buffers are DEVICE pointers owned by the caller; the library allocates nothing and
  *     never synchronises. Its only state is a per-device compute-unit count, the test-only
  *     override below, and the row-claim counters of large launches: a file-scope device
- *     array of 256 counters (64 KiB per device, no allocation), one per stream on first use
- *     and for the life of the process (a new stream that gets a destroyed stream's handle
- *     gets its counter too: hipStreamDestroy completes the stream's pending work first on
- *     ROCm). A launch with claimed rows leaves its counter at 0.
- *     Calls on one stream run one after another and share its counter; calls on different
- *     streams never share one. A call enqueued under stream capture, on the per-thread
- *     default stream, on a stream of another device, or once every counter belongs to
- *     another stream, takes the same kernel with rows by workgroup index instead (the same
- *     outputs, bit for bit).
+ *     array of 256 slots of four 256-byte counters (256 KiB per device, no allocation),
+ *     one slot per stream on first use and for the life of the process (a new stream that
+ *     gets a destroyed stream's handle gets its slot too: hipStreamDestroy completes the
+ *     stream's pending work first on ROCm). A launch with claimed rows leaves its counters
+ *     at 0. Calls on one stream run one after another and share its slot; calls on
+ *     different streams never share one. A call enqueued under stream capture, on the
+ *     per-thread default stream, on a stream of another device, or once every slot
+ *     belongs to another stream, takes the same kernel with rows by workgroup index
+ *     instead (the same outputs, bit for bit).
  *   - `stream` is a hipStream_t (NULL = the legacy default stream). On ARF_OK one kernel
  *     has been enqueued on it (none when tokens == 0; several, in row order, when a
  *     one-row-per-workgroup or one-row-per-wavefront grid would exceed the 2^32 - 1
@@ -206,13 +206,14 @@ int32_t arf_version(void);
  * the current device's compute-unit count and LDS size are queried, which may return
  * ARF_ERR_HIP). out[0] = path: 1 row per wavefront, 2 row per workgroup, 3 held rows (one
  * workgroup per compute unit reads a batch of rows, keeping each row's rounded residual in
- * LDS, then writes their outputs), 4 row per workgroup with the rows past the first two
- * workgroups per compute unit claimed from a counter in the order the workgroups start
- * (two workgroups per compute unit; a call that may not claim, see the conventions above,
- * runs path 2 with a grid of one workgroup per row); out[1] = wavefronts per workgroup;
- * out[2] = 16-byte chunks (8 elements) per lane; out[3] = workgroups in the grid (as an
- * unsigned 32-bit value; path 4: the rows plus max(64, rows/16) workgroups that find no
- * row). Honours arf_set_path_override.
+ * LDS, then writes their outputs), 4 row per workgroup with the rows past the first W
+ * workgroups per compute unit claimed from 1, 2 or 4 counters in the order the
+ * workgroups start (W = 2 workgroups per compute unit, or 4 for rows of less than 96 KiB
+ * of traffic; a call that may not claim, see the conventions above, runs path 2 with a
+ * grid of one workgroup per row); out[1] = wavefronts per workgroup; out[2] = 16-byte
+ * chunks (8 elements) per lane; out[3] = workgroups in the grid (as an unsigned 32-bit
+ * value; path 4: the rows plus max(64, rows/16) workgroups that find no row, rounded up
+ * so that every counter has as many claimants). Honours arf_set_path_override.
  */
 arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
                         int32_t partial_dtype, int32_t num_cus, int32_t* out);
@@ -222,8 +223,9 @@ arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
  * library. path 0 = automatic (the other two arguments must be 0); 1 = one row per
  * wavefront; 2 = one row per workgroup, rows by workgroup index; 3 = held rows (4
  * wavefronts; rows of up to 16384 elements; arf_reduce_rows keeps its automatic plan);
- * 4 = one row per workgroup with EVERY row claimed from the stream's counter (where a call
- * may claim; a grid beyond one dispatch runs path 2). waves_per_block (paths 2 and 4: 4, 8
+ * 4 = one row per workgroup with EVERY row claimed from the stream's counters (4 of them
+ * for rows of less than 96 KiB of traffic, 2 below 256 KiB, else 1; where a call may
+ * claim; a grid beyond one dispatch runs path 2). waves_per_block (paths 2 and 4: 4, 8
  * or 16; paths 1 and 3: 0 or 4) and chunks_per_lane (1, 2, 4 or 8) force the geometry when
  * non-zero. A forced geometry that cannot cover a call's hidden size makes that call return
  * ARF_ERR_VALUE. Returns ARF_ERR_VALUE for values outside these sets.

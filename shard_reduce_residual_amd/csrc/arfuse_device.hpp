@@ -66,10 +66,13 @@ struct Params {
     int32_t reduce_only;       // store the reduced value and stop
     int32_t held_rows;         // held-row kernel: rows a workgroup holds at once (K)
     // Row claims (one row per workgroup only): workgroups with index >= claim_static take
-    // their row from *claim in the order they start; NULL: row = row_begin + workgroup index.
-    uint32_t* claim;           // counter, 0 at launch; the launch leaves it at 0
+    // their row from one of claim_split counters in the order they start; NULL: row =
+    // row_begin + workgroup index.
+    uint32_t* claim;           // counter k at claim + 64 k, each 0 at launch and left at 0
     int64_t claim_static;      // workgroups below this index keep row_begin + index
-    uint32_t claim_count;      // workgroups that claim (gridDim.x - claim_static)
+    uint32_t claim_count;      // workgroups that claim (gridDim.x - claim_static), a
+                               // multiple of 8 << claim_shift
+    uint32_t claim_shift;      // 2^claim_shift counters share the claims (0..2)
 };
 
 struct ActBF16 {};
@@ -373,16 +376,26 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
             // Past the static prefix, rows go to workgroups in the order they start: the
             // rows in flight then stay one compact window of the launch however far the
             // XCDs drift apart, and a faster XCD takes more rows. One relaxed device-scope
-            // increment per workgroup; the launch's last increment returns the counter to 0
-            // for the next launch on the same stream. The grid has claim_count workgroups
-            // past the prefix, more than the rows left: the surplus finds no row and exits.
+            // increment per workgroup. The claims are spread over S = 2^claim_shift
+            // counters, 256 bytes apart, since one counter serves only so many claims per
+            // microsecond: counter k hands out rows k, k + S, k + 2S, ... to the
+            // workgroups i past the prefix with (i / 8) mod S == k, a group of 8
+            // consecutive workgroups (one per XCD) at a time, so that every counter serves
+            // every XCD. Each counter has claim_count / S claimants; the last increment of
+            // each returns it to 0 for the next launch on the same stream. The claimants
+            // outnumber the rows left: the surplus finds no row and exits. (Shifts, not a
+            // division by S: the claim is on the workgroup's critical path.)
             __shared__ int64_t s_row;
             if (threadIdx.x == 0) {
-                const uint32_t c = __hip_atomic_fetch_add(p.claim, 1u, __ATOMIC_RELAXED,
+                const uint32_t sh = p.claim_shift;
+                const uint32_t i = blockIdx.x - (uint32_t)p.claim_static;
+                const uint32_t k = (i >> 3) & ((1u << sh) - 1u);
+                uint32_t* ctr = p.claim + k * 64u;
+                const uint32_t c = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED,
                                                           __HIP_MEMORY_SCOPE_AGENT);
-                if (c == p.claim_count - 1u)
-                    __hip_atomic_store(p.claim, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                s_row = p.claim_static + (int64_t)c;
+                if (c == (p.claim_count >> sh) - 1u)
+                    __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_row = p.claim_static + (int64_t)(((uint64_t)c << sh) + k);
             }
             __syncthreads();
             row = p.row_begin + s_row;

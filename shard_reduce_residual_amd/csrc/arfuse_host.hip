@@ -44,7 +44,8 @@ struct Plan {
     int held;      // held-row kernel: rows per workgroup and phase
     uint32_t lds;  // dynamic LDS bytes per workgroup (held rows; the occupancy cap of path 4)
     int64_t claim_static;   // path 4: workgroups that keep the row of their index
-    uint32_t claim_count;   // path 4: workgroups that claim a row
+    uint32_t claim_count;   // path 4: workgroups that claim a row (a multiple of 8 * split)
+    int claim_split;        // path 4: counters the claims are spread over (1, 2 or 4)
 };
 
 struct DeviceInfo {
@@ -55,14 +56,16 @@ struct DeviceInfo {
 
 // ---- row-claim counters -------------------------------------------------------------------
 //
-// Path 4 hands rows to workgroups from a device counter that every launch returns to 0. The
-// counters are this file-scope array, one 256-byte line each (so no two share a cache line
-// or an atomic unit's queue), on every device the library runs on; nothing is allocated.
-// A counter belongs to one stream: calls on one stream run one after another, so they may
-// share it, and calls on different streams, which may overlap, never do. Calls that must
-// not claim (see claim_counter) take the same kernel with rows by workgroup index.
+// Path 4 hands rows to workgroups from up to kMaxSplit device counters that every launch
+// returns to 0. The counters are this file-scope array, on every device the library runs
+// on; nothing is allocated. A slot holds one stream's counters, one 256-byte line each (so
+// no two share a cache line or an atomic unit's queue). A slot belongs to one stream: calls
+// on one stream run one after another, so they may share it, and calls on different
+// streams, which may overlap, never do. Calls that must not claim (see claim_counter) take
+// the same kernel with rows by workgroup index.
 constexpr int kClaimSlots = 256;
-constexpr int kSlotWords = 64;
+constexpr int kMaxSplit = 4;
+constexpr int kSlotWords = 64 * kMaxSplit;
 static __device__ __align__(256) uint32_t scratch[kClaimSlots * kSlotWords];
 
 struct ClaimTable {
@@ -73,7 +76,7 @@ struct ClaimTable {
 };
 ClaimTable g_claims;
 
-// The counter of `stream` on device `dev`, or NULL when the call must not claim rows:
+// The counters of `stream` on device `dev`, or NULL when the call must not claim rows:
 //  * the stream is being captured: a captured graph may be replayed on another stream;
 //  * the per-thread default stream: one handle stands for a different stream per thread;
 //  * the stream belongs to another device than the current one;
@@ -164,12 +167,20 @@ bool held_plan(int64_t rows, int32_t hidden, const DeviceInfo& dev, int chunks, 
 //    measured it faster: 4 wavefronts per row, and either at least 16 rows per compute unit
 //    with at least 128 KiB of traffic per row, or at least 8 rows per compute unit with at
 //    least 256 KiB per row: 1-8% faster (8 shards of 8192 x 16384 with per-token fp8:
-//    512-528 -> 481-487 us). With less traffic per row the launch claims rows faster than
-//    one counter serves them (beyond ~50 per microsecond), and with fewer rows per compute
-//    unit there is little drift to correct; there it was up to 8% slower. Two workgroups
-//    per compute unit (an LDS reservation caps them) measured faster than three with claims
-//    on every shape; the first two workgroups per compute unit keep their own row, so the
-//    launch's first wave of workgroups does not queue on the counter at once.
+//    512-528 -> 481-487 us). With fewer rows per compute unit there is little drift to
+//    correct. Two workgroups per compute unit (an LDS reservation caps them) measured
+//    faster than three with claims on every shape; the first two workgroups per compute
+//    unit keep their own row, so the launch's first wave of workgroups does not queue on
+//    the counter at once.
+//  * one counter serves about 50 claims per microsecond; shorter rows claim faster than
+//    that, so their claims are spread over 2 or 4 counters (a sweep of 22 shapes, 2-16
+//    shards, hidden 2048-16384, against rows by index, row per wavefront and one counter):
+//    rows of 128-256 KiB take 2 counters (up to 1.6% faster than one; at 256 KiB and more
+//    one counter stays as fast); from 32 rows per compute unit, rows of 96-128 KiB take 2
+//    counters and 2 workgroups per compute unit (4 x 16384 x 8192: -3%), rows of 32-96 KiB
+//    with at least 256 chunks take 4 counters and 4 workgroups per compute unit (8 x 16384
+//    x 4096: -6%; 16 x 16384 x 2048: -9% against one row per wavefront). Rows of 28 KiB
+//    and launches of 16 rows per compute unit gained nothing and keep their plans.
 bool held_wins(int64_t tokens, int32_t hidden, int n, int quant, const DeviceInfo& dev,
                Plan* pl) {
     if (n > 4 || hidden < 4096 || hidden > 8192 || quant != arf::kQuantNone ||
@@ -182,11 +193,29 @@ bool held_wins(int64_t tokens, int32_t hidden, int n, int quant, const DeviceInf
     return true;
 }
 
-// The claim rule of the plan (path 4), from the launch-geometry notes above.
-bool claim_wins(int64_t tokens, int64_t row_bytes, int waves, const DeviceInfo& dev) {
-    if (waves != 4) return false;
-    return (tokens >= 16LL * dev.cus && row_bytes >= 128 * 1024) ||
-           (tokens >= 8LL * dev.cus && row_bytes >= 256 * 1024);
+// The claim rules of the plan (path 4), from the launch-geometry notes above: the counters
+// the claims are spread over (0: rows by index) and the workgroups per compute unit.
+struct ClaimRule {
+    int split;
+    int per_cu;
+};
+ClaimRule claim_rule(int64_t tokens, int64_t row_bytes, int hc, int waves, const DeviceInfo& dev) {
+    if (waves != 4) return {0, 0};
+    if ((tokens >= 16LL * dev.cus && row_bytes >= 128 * 1024) ||
+        (tokens >= 8LL * dev.cus && row_bytes >= 256 * 1024))
+        return {row_bytes >= 256 * 1024 ? 1 : 2, 2};
+    if (tokens >= 32LL * dev.cus && hc >= 256 && row_bytes >= 32 * 1024) {
+        if (row_bytes >= 96 * 1024) return {2, 2};
+        return {4, 4};
+    }
+    return {0, 0};
+}
+
+// Forced claims (tests): the split of the plan's rules for the row size.
+ClaimRule forced_claim_rule(int64_t row_bytes) {
+    return row_bytes < 96 * 1024    ? ClaimRule{4, 4}
+           : row_bytes < 256 * 1024 ? ClaimRule{2, 2}
+                                    : ClaimRule{1, 2};
 }
 
 // Static LDS of the fused kernel (per-wavefront partial sums and maxima, the claimed row),
@@ -203,6 +232,7 @@ arf_status make_plan(int64_t tokens, int32_t hidden, int n, int quant, int64_t r
     pl->lds = 0;
     pl->claim_static = 0;
     pl->claim_count = 0;
+    pl->claim_split = 0;
     if (path == 3) {
         // the held-row kernel has no reduce-only form: such calls take the default plan
         if (!reduce_only) return held_plan(tokens, hidden, dev, chunks, pl) ? ARF_OK : ARF_ERR_VALUE;
@@ -210,18 +240,20 @@ arf_status make_plan(int64_t tokens, int32_t hidden, int n, int quant, int64_t r
     }
     if (path == 0 && !reduce_only && held_wins(tokens, hidden, n, quant, dev, pl)) return ARF_OK;
     const bool forced_claims = path == 4;
-    bool claims = forced_claims;
+    ClaimRule rule = forced_claims ? forced_claim_rule(row_bytes) : ClaimRule{0, 0};
     if (path == 0) {
         waves = chunks = 0;
         const bool many_rows = tokens >= 2LL * num_cus;
-        if ((hc <= 128 && many_rows) || (hc <= 256 && tokens >= 8LL * num_cus)) {
+        rule = claim_rule(tokens, row_bytes, hc, 4, dev);
+        if (rule.split == 0 &&
+            ((hc <= 128 && many_rows) || (hc <= 256 && tokens >= 8LL * num_cus))) {
             path = 1;
         } else {
             path = 2;
             waves = many_rows ? 4 : 8;
             if (hc > waves * 64 * 8) waves = 16;
             chunks = pow2_at_least(div_up(hc, waves * 64));
-            claims = claim_wins(tokens, row_bytes, waves, dev);
+            if (waves != 4) rule = ClaimRule{0, 0};
         }
     }
     if (path == 1) {
@@ -241,18 +273,25 @@ arf_status make_plan(int64_t tokens, int32_t hidden, int n, int quant, int64_t r
         if (chunks > 8 || waves * 64 * chunks < hc) return ARF_ERR_VALUE;
         pl->grid = (uint32_t)tokens;
         path = 2;
-        if (claims) {
-            // forced (tests): every row is claimed; planned: the first two workgroups per
-            // compute unit keep their row. One claiming workgroup per 16 rows (at least 64)
-            // beyond the rows is the slack that lets a faster XCD take more rows.
-            const int64_t first = forced_claims ? 0 : std::min<int64_t>(tokens, 2LL * num_cus);
-            const int64_t grid = tokens + std::max<int64_t>(64, tokens / 16);
+        if (rule.split > 0) {
+            // forced (tests): every row is claimed; planned: the first per_cu workgroups
+            // per compute unit keep their row. One claiming workgroup per 16 rows (at
+            // least 64) beyond the rows is the slack that lets a faster XCD take more
+            // rows; the claimants are a multiple of 8 * split, so that every counter has
+            // as many as the others.
+            const int64_t first =
+                forced_claims ? 0 : std::min<int64_t>(tokens, (int64_t)rule.per_cu * num_cus);
+            const int64_t unit = 8LL * rule.split;
+            const int64_t count =
+                div_up(tokens - first + std::max<int64_t>(64, tokens / 16), unit) * unit;
+            const int64_t grid = first + count;
             if (grid * 64 * waves <= (int64_t)UINT32_MAX) {   // one dispatch, else path 2
                 path = 4;
                 pl->claim_static = first;
-                pl->claim_count = (uint32_t)(grid - first);
+                pl->claim_count = (uint32_t)count;
+                pl->claim_split = rule.split;
                 pl->grid = (uint32_t)grid;
-                pl->lds = (uint32_t)((dev.lds - kStaticLdsSlack) / 2);
+                pl->lds = (uint32_t)((dev.lds - kStaticLdsSlack) / rule.per_cu);
             }
         }
     }
@@ -468,12 +507,14 @@ arf_status run(Call c, void* stream) {
     p.claim = nullptr;
     p.claim_static = 0;
     p.claim_count = 0;
+    p.claim_shift = 0;
     if (hfn)   // at most one workgroup per compute unit, looping over its rows
         return hfn(p, pl.grid, pl.lds, (hipStream_t)stream) == hipSuccess ? ARF_OK : ARF_ERR_HIP;
     if (pl.path == 4) {   // one dispatch (the plan checked its size)
         p.claim = counter;
         p.claim_static = pl.claim_static;
         p.claim_count = pl.claim_count;
+        p.claim_shift = pl.claim_split == 4 ? 2u : pl.claim_split == 2 ? 1u : 0u;
         return fn(p, pl.grid, pl.lds, (hipStream_t)stream) == hipSuccess ? ARF_OK : ARF_ERR_HIP;
     }
     // One dispatch covers at most 2^32 - 1 work-items: a grid that would exceed that is

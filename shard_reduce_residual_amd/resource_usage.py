@@ -8,8 +8,8 @@ For each of the five workloads (and the fp8/MXFP4 variants, which share their ke
 the plan's geometry is mapped to its kernel instantiation, whose metadata gives arch
 VGPRs, AGPRs, SGPRs, spills, static LDS and private (scratch) bytes. The held-row kernel's
 LDS is dynamic and follows the plan (held rows x (hidden*2 + 12 per wavefront)); path 4
-(claimed rows) reserves (160 KiB - 2 KiB) / 2 of dynamic LDS per workgroup, which caps it
-at two workgroups per CU. Occupancy on gfx950: a SIMD has 512 registers per lane shared by
+(claimed rows) reserves (160 KiB - 2 KiB) / W of dynamic LDS per workgroup, which caps it
+at W workgroups per CU (W = 4 for rows of less than 96 KiB of traffic, else 2). Occupancy on gfx950: a SIMD has 512 registers per lane shared by
 its waves (allocated in blocks of 8), at most 8 waves per SIMD, 4 SIMDs and 160 KiB of LDS
 per CU.
 """
@@ -114,7 +114,9 @@ def report(cus: int = 256) -> str:
                     plan["waves"], "true" if plan["path"] == 1 else "false"))]
             assert len(cand) == 1, cand
             name = cand[0]
-            dyn = (LDS_PER_CU - 2048) // 2 if plan["path"] == 4 else 0
+            row_bytes = w.n_shards * w.hidden * w.sp + 6 * w.hidden
+            per_cu = 4 if row_bytes < 96 * 1024 else 2
+            dyn = (LDS_PER_CU - 2048) // per_cu if plan["path"] == 4 else 0
         m = cache[tu][name]
         regs = m["vgpr_count"]            # on gfx950: arch VGPRs + AGPRs, as allocated
         agpr = m["agpr_count"]

@@ -135,20 +135,28 @@ int main() {
                     EXPECT(o[0] == 2 ? (o[1] == 4 || o[1] == 8 || o[1] == 16) : o[1] == 4);
                     EXPECT(lanes * o[2] * 8 >= h);
                     // held rows: one workgroup per compute unit, the whole launch in one batch
-                    // of at most 160 KiB of LDS per workgroup; claimed rows: the rows plus
-                    // max(64, rows/16) in one dispatch
+                    // of at most 160 KiB of LDS per workgroup; claimed rows: a static prefix
+                    // of per_cu workgroups per CU, then claimants for the rows left plus
+                    // max(64, rows/16), rounded up to a multiple of 8 * split, in one dispatch
                     const int64_t surplus = t / 16 > 64 ? t / 16 : 64;
-                    const int64_t g = o[0] == 1 ? (t + 3) / 4
-                                      : o[0] == 2 ? t
-                                      : o[0] == 4 ? t + surplus
-                                                  : (t < cus ? t : cus);
-                    EXPECT((int64_t)(uint32_t)o[3] == g);
+                    int64_t g = o[0] == 1 ? (t + 3) / 4 : o[0] == 2 ? t : (t < cus ? t : cus);
                     if (o[0] == 4) {
                         const int64_t row_bytes = (int64_t)n * h * 2 + 6LL * h;
-                        EXPECT((t >= 16LL * cus && row_bytes >= 128 * 1024) ||
-                               (t >= 8LL * cus && row_bytes >= 256 * 1024));
+                        int split = 0, per_cu = 0;
+                        if ((t >= 16LL * cus && row_bytes >= 128 * 1024) ||
+                            (t >= 8LL * cus && row_bytes >= 256 * 1024)) {
+                            split = row_bytes >= 256 * 1024 ? 1 : 2; per_cu = 2;
+                        } else if (t >= 32LL * cus && h / 8 >= 256 && row_bytes >= 32 * 1024) {
+                            split = row_bytes >= 96 * 1024 ? 2 : 4;
+                            per_cu = split;
+                        }
+                        EXPECT(split > 0);
+                        const int64_t first = t < (int64_t)per_cu * cus ? t : (int64_t)per_cu * cus;
+                        const int64_t unit = 8LL * (split > 0 ? split : 1);
+                        g = first + div_up_i64(t - first + surplus, unit) * unit;
                         EXPECT(g * 256 <= (int64_t)UINT32_MAX);
                     }
+                    EXPECT((int64_t)(uint32_t)o[3] == g);
                     // every launch of one row per workgroup or wavefront fits the work-item
                     // limit of one dispatch, or is split by the caller into row ranges
                     if (o[0] != 2 && o[0] != 1) EXPECT((int64_t)(uint32_t)o[3] * lanes <= (int64_t)UINT32_MAX);
@@ -180,9 +188,12 @@ int main() {
     EXPECT(arf_set_path_override(3, 4, 2) == ARF_OK);
     EXPECT(arf_get_plan(8, 100, 4096, ARF_BF16, 256, o) == ARF_OK && o[0] == 3 && o[2] == 2);
     EXPECT(arf_get_plan(8, 100, 4104, ARF_BF16, 256, o) == ARF_ERR_VALUE);
-    // claimed rows forced: every row claimed, any row count; beyond one dispatch, path 2
+    // claimed rows forced: every row claimed, any row count (claimants rounded up to a
+    // multiple of 8 * split: 4 counters below 96 KiB per row, 2 below 256 KiB, else 1);
+    // beyond one dispatch, path 2
     EXPECT(arf_set_path_override(4, 0, 0) == ARF_OK);
-    EXPECT(arf_get_plan(8, 100, 4096, ARF_BF16, 256, o) == ARF_OK && o[0] == 4 && o[1] == 4 && o[2] == 2 && o[3] == 164);
+    EXPECT(arf_get_plan(8, 100, 4096, ARF_BF16, 256, o) == ARF_OK && o[0] == 4 && o[1] == 4 && o[2] == 2 && o[3] == 192);
+    EXPECT(arf_get_plan(8, 100, 8192, ARF_BF16, 256, o) == ARF_OK && o[0] == 4 && o[1] == 4 && o[2] == 4 && o[3] == 176);
     EXPECT(arf_get_plan(8, 0, 4096, ARF_BF16, 256, o) == ARF_OK && o[0] == 4 && o[3] == 64);
     EXPECT(arf_get_plan(8, (int64_t(1) << 31) - 1, 4096, ARF_BF16, 256, o) == ARF_OK && o[0] == 2);
     EXPECT(arf_get_plan(8, 100, 18016, ARF_BF16, 256, o) == ARF_OK && o[0] == 4 && o[1] == 16 && o[2] == 4);
@@ -198,7 +209,12 @@ int main() {
     EXPECT(arf_get_plan(8, 8192, 16384, ARF_BF16, 256, o) == ARF_OK && o[0] == 4 && o[1] == 4 && o[2] == 8 && o[3] == 8704);
     EXPECT(arf_get_plan(8, 2047, 16384, ARF_BF16, 256, o) == ARF_OK && o[0] == 2);
     EXPECT(arf_get_plan(8, 4096, 8192, ARF_BF16, 256, o) == ARF_OK && o[0] == 4);
-    EXPECT(arf_get_plan(8, 8192, 4096, ARF_BF16, 256, o) == ARF_OK && o[0] == 2);
+    EXPECT(arf_get_plan(8, 8191, 4096, ARF_BF16, 256, o) == ARF_OK && o[0] == 2);
+    EXPECT(arf_get_plan(8, 8192, 4096, ARF_BF16, 256, o) == ARF_OK && o[0] == 4 && o[3] == 8704);
+    EXPECT(arf_get_plan(8, 8192, 2048, ARF_BF16, 256, o) == ARF_OK && o[0] == 4 && o[2] == 1 && o[3] == 8704);
+    EXPECT(arf_get_plan(4, 16384, 2048, ARF_BF16, 256, o) == ARF_OK && o[0] == 1);   // 28 KiB per row
+    EXPECT(arf_get_plan(16, 16384, 1024, ARF_BF16, 256, o) == ARF_OK && o[0] == 1);  // 128 chunks
+    EXPECT(arf_get_plan(4, 8192, 8192, ARF_BF16, 256, o) == ARF_OK && o[0] == 4 && o[3] == 8704);
     EXPECT(arf_get_plan(4, 8192, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 4 && o[3] == 8704);
     // held rows by default only in their measured range
     EXPECT(arf_get_plan(4, 2048, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 3 && o[2] == 4 && o[3] == 256);

@@ -128,9 +128,10 @@ def test_plan_covers_the_row_and_follows_the_menu():
                         assert p["waves"] == 4 and p["grid"] == (t + 3) // 4
                     elif p["path"] == 2:
                         assert p["waves"] in (4, 8, 16) and p["grid"] == t
-                    elif p["path"] == 4:   # claimed rows: the rows plus the surplus
-                        assert p["waves"] == 4 and p["grid"] == t + max(64, t // 16)
-                        assert t >= 8 * 256
+                    elif p["path"] == 4:   # claimed rows: the rows plus the surplus,
+                        # rounded up to a multiple of 8 * split (split 2 or 4)
+                        assert p["waves"] == 4 and t >= 8 * 256
+                        assert 0 <= p["grid"] - (t + max(64, t // 16)) < 32
                     else:   # held rows: one workgroup per CU, one batch of rows each
                         assert p["path"] == 3 and n <= 4 and p["waves"] == 4
                         assert p["grid"] == min(t, 256) and 6 * 256 <= t <= 16 * 256
@@ -157,9 +158,12 @@ def test_plan_row_per_wave_region():
     assert plan(8, 511, 1024)["path"] == 2 and plan(8, 512, 1024)["path"] == 1
     assert plan(8, 8192, 1024) == {"path": 1, "waves": 4, "chunks": 2, "grid": 2048}
     assert plan(8, 2047, 2048)["path"] == 2 and plan(8, 2048, 2048)["path"] == 1
-    assert plan(8, 8192, 2048) == {"path": 1, "waves": 4, "chunks": 4, "grid": 2048}
-    assert plan(4, 8192, 2056, 2)["path"] == 2          # 257 chunks
-    for t in (512, 1024, 2048, 8192):
+    assert plan(8, 8191, 2048) == {"path": 1, "waves": 4, "chunks": 4, "grid": 2048}
+    assert plan(4, 16384, 2048)["path"] == 1            # 28 KiB per row: no claims
+    assert plan(16, 16384, 1024)["path"] == 1           # 128 chunks: no claims
+    assert plan(4, 8191, 2056, 2)["path"] == 2          # 257 chunks
+    assert plan(4, 8192, 2056, 2)["path"] == 4          # 257 chunks, claimed from 32 per CU
+    for t in (512, 1024, 2048, 4096, 8191):
         assert plan(8, t, 4096)["path"] == 2
     # the thresholds scale with the CU count
     assert plan(8, 1023, 2048, 0, 128)["path"] == 2 and plan(8, 1024, 2048, 0, 128)["path"] == 1
@@ -186,7 +190,13 @@ def test_plan_claim_region():
     assert plan(8, 4095, 8192)["path"] == 2 and plan(8, 4096, 8192)["path"] == 4
     assert plan(1, 4096, 16384)["path"] == 4 and plan(1, 4096, 16376)["path"] == 2
     assert plan(8, 2047, 16384)["path"] == 2 and plan(8, 2048, 16384)["path"] == 4
-    assert plan(8, 8192, 4096)["path"] == 2            # 88 KiB per row
+    # rows of 32-128 KiB from 32 rows per CU, the claims spread over 4 counters (below 96
+    # KiB, 4 workgroups per CU) or 2 (2 per CU): 88, 44 and 112 KiB per row
+    assert plan(8, 8191, 4096)["path"] == 2
+    assert plan(8, 8192, 4096) == {"path": 4, "waves": 4, "chunks": 2, "grid": 8192 + 512}
+    assert plan(8, 8192, 2048) == {"path": 4, "waves": 4, "chunks": 1, "grid": 8192 + 512}
+    assert plan(4, 8192, 8192) == {"path": 4, "waves": 4, "chunks": 4, "grid": 8192 + 512}
+    assert plan(4, 16383, 2048)["path"] == 1            # 28 KiB per row
     assert plan(5, 4096, 7168, 2) == {"path": 4, "waves": 4, "chunks": 4, "grid": 4096 + 256}
     assert plan(8, 8192, 65536)["path"] == 2           # 16 wavefronts
     assert plan(8, 64 * 1024, 16384)["grid"] == 64 * 1024 + 4096
@@ -211,10 +221,11 @@ def test_path_override_forces_and_rejects():
         arf.arf_set_path_override(3, 4, 4)
         assert plan(8, 100, 4096) == {"path": 3, "waves": 4, "chunks": 4, "grid": 100}
         arf.arf_set_path_override(4)     # every row claimed, any size
-        assert plan(8, 100, 4096) == {"path": 4, "waves": 4, "chunks": 2, "grid": 164}
+        # claimants rounded up to a multiple of 8 * split: 4 counters below 96 KiB per row
+        assert plan(8, 100, 4096) == {"path": 4, "waves": 4, "chunks": 2, "grid": 192}
         assert plan(8, 8192, 1024)["path"] == 4
         arf.arf_set_path_override(4, 8, 0)
-        assert plan(8, 3, 16384) == {"path": 4, "waves": 8, "chunks": 4, "grid": 67}
+        assert plan(8, 3, 16384) == {"path": 4, "waves": 8, "chunks": 4, "grid": 72}
         for bad in ((5, 0, 0), (0, 4, 0), (2, 3, 0), (2, 2, 0), (2, 4, 3), (1, 8, 0), (3, 8, 0),
                     (4, 2, 0), (4, 4, 3)):
             with pytest.raises(arf.ArfError):

@@ -898,6 +898,25 @@ def test_claim_plan_fp32_partials_every_row():
     compare(got, ref, "4 x 4096 x 7168 f32, claimed rows")
 
 
+@pytest.mark.parametrize("shape", [(8, 8192, 2048, "bf16", "per_token"),
+                                   (4, 8192, 8192, "bf16", None)])
+def test_split_claim_plans_every_row(shape):
+    # shapes the plan sends to claims spread over several counters: 44 KiB rows (4
+    # counters, 4 workgroups per CU, the first 1024 workgroups keep their row) and 112 KiB
+    # rows (2 counters, 2 per CU); every row against the oracle, twice on one stream (the
+    # second call finds the counters the first left at 0)
+    n, t, h, pd, quant = shape
+    w = _case(n, t, h, pd, "bf16", 614, quant=quant)
+    plan = arf.arf_get_plan(n, t, h, 0)
+    assert plan["path"] == 4 and plan["grid"] == t + 512, plan
+    say("split claims %s" % (shape,))
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    ref = run_oracle(p, r, g, w.eps, pd, "bf16", quant=quant)
+    for k in range(2):
+        got = run_gpu(pd_, rd, gd, w.eps, "bf16", quant=quant)
+        compare(got, ref, "%s, call %d" % (shape, k))
+
+
 # ---- HIP graph capture --------------------------------------------------------------------
 
 @pytest.mark.parametrize("path", [0, 4])
