@@ -43,8 +43,14 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
     jobs = jobs or max(1, min(len(srcs), os.cpu_count() or 1, 16))
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))
+    # export the C ABI (arf_*) only: the kernels' launchers and host stubs stay local, so
+    # the library cannot clash with another one that instantiates the same templates
+    vmap = os.path.join(OBJDIR, "exports.map")
+    with open(vmap, "w") as f:
+        f.write("{\n  global: arf_*;\n  local: *;\n};\n")
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,--version-script=" + vmap,
+           "-o", tmp] + objs
     subprocess.run(cmd, check=True, capture_output=True)
     os.replace(tmp, LIB)
     if verbose:

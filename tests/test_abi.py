@@ -33,6 +33,19 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(arf.SIGNATURES)
 
 
+def test_library_exports_nothing_else():
+    # the dynamic symbol table holds the C ABI only (the build's version script keeps the
+    # kernels' launchers and host stubs local)
+    import shutil
+    import subprocess
+    if not shutil.which("nm"):
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-D", "--defined-only", arf.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    names = sorted(line.split()[-1] for line in out.splitlines() if line.strip())
+    assert names == declared_symbols(), names[:20]
+
+
 def test_version_and_status_strings():
     assert arf.arf_version() == 300
     for code, name in enumerate(arf.STATUS):
