@@ -215,6 +215,7 @@ static void cpu_checks(void) {
     CHECK(arf_set_path_override(0, 0, 0) == ARF_OK, "override reset");
     int32_t plan[4] = {0, 0, 0, 0};
     CHECK(arf_get_plan(8, 8192, 16384, ARF_BF16, 256, plan) == ARF_OK && plan[0] == 4, "plan of 8 x 8192 x 16384");
+    CHECK(arf_get_plan(8, 8192, 2048, ARF_BF16, 256, plan) == ARF_OK && plan[0] == 4, "plan of 8 x 8192 x 2048");
 }
 
 int main(int argc, char** argv) {
@@ -230,6 +231,7 @@ int main(int argc, char** argv) {
             {"bf16, per-token fp8, own stream", 8, 4096, ARF_BF16, ARF_BF16, ARF_QUANT_PER_TOKEN, 300, 0, 1, 202},
             {"fp32 partials 2048 x 7168, in place (held rows)", 4, 7168, ARF_F32, ARF_BF16, -1, 2048, 1, 0, 303},
             {"bf16 2048 x 16384, per-token fp8, own stream (claimed rows)", 8, 16384, ARF_BF16, ARF_BF16, ARF_QUANT_PER_TOKEN, 2048, 0, 1, 404},
+            {"bf16 8192 x 2048, per-token fp8, own stream (claims over 4 counters)", 8, 2048, ARF_BF16, ARF_BF16, ARF_QUANT_PER_TOKEN, 8192, 0, 1, 505},
         };
         for (size_t i = 0; i < sizeof(cases) / sizeof(cases[0]); ++i) {
             printf("running %s\n", cases[i].name);

@@ -32,7 +32,7 @@ def test_c_consumer_on_the_gpu():
     r = subprocess.run([exe, "gpu"], capture_output=True, text=True, timeout=300)
     print(r.stdout)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok gpu"), r.stdout[-4000:] + r.stderr[-4000:]
-    assert r.stdout.count("case ") == 4, r.stdout
+    assert r.stdout.count("case ") == 5, r.stdout
 
 
 def test_header_is_strict_c(tmp_path):
