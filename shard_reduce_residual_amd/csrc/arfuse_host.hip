@@ -147,12 +147,15 @@ bool held_plan(int64_t rows, int32_t hidden, const DeviceInfo& dev, int chunks, 
 // bf16 shards and 4 fp32 shards, and checked on other shapes (hidden 1536..12288, 4 and 16
 // bf16, 8 fp16 and 2 fp32 shards), where it stays within 1.1% of the best menu entry on
 // geometric mean:
-//  * one row per wavefront (4 rows per workgroup) for short rows once the grid is large
-//    enough to fill the chip: rows of <= 128 chunks from 2 rows per compute unit, rows of
-//    <= 256 chunks from 8 rows per compute unit;
+//  * one row per wavefront (4 rows per workgroup) for short rows: rows of <= 64 chunks
+//    always, rows of <= 128 chunks from 2 rows per compute unit, rows of <= 256 chunks from
+//    8 rows per compute unit;
 //  * otherwise one row per workgroup:
-//    - few rows (< 2 per compute unit): 8 wavefronts per row, so that each row exposes
-//      more parallel loads;
+//    - few rows (< 2 per compute unit) of more than 256 chunks: 8 wavefronts per row, so
+//      that each row exposes more parallel loads; rows of up to 256 chunks fill no more
+//      than 4 wavefronts' lanes, and 4 wavefronts measured 6-22% faster than 8 there
+//      (graph replay of 1-511 rows, hidden 512-2048, 2 and 8 shards; one row per
+//      wavefront 13-35% faster still for 64-chunk rows);
 //    - otherwise 4 wavefronts with up to 8 chunks per lane, so that several rows share a
 //      compute unit;
 //    - rows too wide for 8 chunks per lane use 16 wavefronts.
@@ -245,12 +248,12 @@ arf_status make_plan(int64_t tokens, int32_t hidden, int n, int quant, int64_t r
         waves = chunks = 0;
         const bool many_rows = tokens >= 2LL * num_cus;
         rule = claim_rule(tokens, row_bytes, hc, 4, dev);
-        if (rule.split == 0 &&
-            ((hc <= 128 && many_rows) || (hc <= 256 && tokens >= 8LL * num_cus))) {
+        if (rule.split == 0 && (hc <= 64 || (hc <= 128 && many_rows) ||
+                                (hc <= 256 && tokens >= 8LL * num_cus))) {
             path = 1;
         } else {
             path = 2;
-            waves = many_rows ? 4 : 8;
+            waves = many_rows || hc <= 256 ? 4 : 8;
             if (hc > waves * 64 * 8) waves = 16;
             chunks = pow2_at_least(div_up(hc, waves * 64));
             if (waves != 4) rule = ClaimRule{0, 0};
@@ -537,15 +540,16 @@ arf_status run(Call c, void* stream) {
 __global__ __launch_bounds__(256) void e4m3_encode_kernel(const float* __restrict__ in,
                                                           uint8_t* __restrict__ out,
                                                           int64_t n) {
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i >= n) return;
-    float v[4];
+    for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n;
+         i += (int64_t)gridDim.x * 256 * 4) {
+        float v[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = i + k < n ? in[i + k] : 0.0f;
-    const uint32_t w = arf::e4m3x4(v[0], v[1], v[2], v[3]);
+        for (int k = 0; k < 4; ++k) v[k] = i + k < n ? in[i + k] : 0.0f;
+        const uint32_t w = arf::e4m3x4(v[0], v[1], v[2], v[3]);
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-        if (i + k < n) out[i + k] = (uint8_t)(w >> (8 * k));
+        for (int k = 0; k < 4; ++k)
+            if (i + k < n) out[i + k] = (uint8_t)(w >> (8 * k));
+    }
 }
 
 // Contiguous spans of 256 lanes x 8 x 16 bytes per workgroup iteration, through a buffer
@@ -739,8 +743,9 @@ arf_status arf_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* strea
     if (!in || !out) return ARF_ERR_NULL;
     if (!aligned(in, 4)) return ARF_ERR_ALIGN;
     if (overlap(span(in, n * 4), span(out, n))) return ARF_ERR_ALIAS;
-    const int64_t blocks = (n + 1023) / 1024;
-    if (blocks > INT32_MAX) return ARF_ERR_SHAPE;
+    // 1024 elements per workgroup and pass; the kernel loops when the grid is capped at
+    // one dispatch's 2^32 - 1 work-items
+    const int64_t blocks = std::min<int64_t>((n + 1023) / 1024, (int64_t)UINT32_MAX / 256);
     void* args[] = {&in, &out, &n};
     return hipLaunchKernel(reinterpret_cast<const void*>(&e4m3_encode_kernel),
                            dim3((uint32_t)blocks), dim3(256), args, 0,
@@ -787,7 +792,9 @@ arf_status arf_stream_mix(void* dst, int64_t write_bytes, const void* src, int64
     int cus = 0;
     arf_status st = device_cus(&cus);
     if (st != ARF_OK) return st;
-    const uint32_t grid = (uint32_t)units;
+    // one workgroup per unit, capped at one dispatch's 2^32 - 1 work-items (the kernel
+    // loops over the units)
+    const uint32_t grid = (uint32_t)std::min<int64_t>(units, (int64_t)UINT32_MAX / 256);
     char* d = (char*)dst;
     const char* sp = (const char*)src;
     void* args[] = {&d, &write_bytes, &sp, &read_bytes, &units};

@@ -165,6 +165,17 @@ def test_plan_for_the_named_workloads():
     assert plan(8, 8192, 65536) == {"path": 2, "waves": 16, "chunks": 8, "grid": 8192}
 
 
+def test_plan_few_rows():
+    # fewer than 2 rows per CU: rows of <= 64 chunks one per wavefront, rows of <= 256
+    # chunks 4 wavefronts per row (more would leave lanes idle), wider rows 8 wavefronts
+    assert plan(2, 16, 1024) == {"path": 2, "waves": 4, "chunks": 1, "grid": 16}
+    assert plan(8, 100, 2048) == {"path": 2, "waves": 4, "chunks": 1, "grid": 100}
+    assert plan(8, 100, 2056) == {"path": 2, "waves": 8, "chunks": 1, "grid": 100}
+    assert plan(8, 16, 512) == {"path": 1, "waves": 4, "chunks": 1, "grid": 4}
+    assert plan(8, 1, 8) == {"path": 1, "waves": 4, "chunks": 1, "grid": 1}
+    assert plan(8, 128, 4096)["waves"] == 8 and plan(8, 64, 8192)["waves"] == 8
+
+
 def test_plan_row_per_wave_region():
     # one row per wavefront: rows of <= 128 chunks from 2 rows per CU, rows of <= 256
     # chunks from 8 rows per CU; never for wider rows
