@@ -582,7 +582,8 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
 
 // ---- the held-row kernel ----------------------------------------------------------------
 //
-// Persistent workgroups (at most one per compute unit), each owning whole rows. A workgroup
+// Persistent workgroups (at most one per compute unit, of 4 or 8 wavefronts: WAVES / 4 per
+// SIMD), each owning whole rows. A workgroup
 // works in batches of up to K rows:
 //  * read half: it streams its rows (shards shard-major, then the residual; the first D-1
 //    shards of the next row are loaded while the current row finishes) and keeps each row's
@@ -605,7 +606,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_reduce_add_rmsnorm(Params p)
 // squares and K*WAVES fp32 maxima. Only hidden/8 <= C * WAVES * 64 is supported (the host
 // checks).
 template <class PT, class AT, int N, int C, int WAVES, bool QUANT>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
 void fused_held_rows(Params p) {
     constexpr int PW = PartTraits<PT>::kPieces;
     constexpr int G = WAVES * 64;              // lanes per row

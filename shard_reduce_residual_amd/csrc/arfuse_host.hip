@@ -112,28 +112,29 @@ uint32_t* claim_counter(int dev, void* stream) {
     return nullptr;
 }
 
-// Held-row kernel geometry: 4 wavefronts, one workgroup per compute unit, each holding up to
-// as many rows as its LDS takes (the row's residual plus 12 bytes per wavefront for the
-// partial sums of squares and the per-token maxima). Rows are spread evenly over the
-// phases. Returns false when the row does not fit the kernel's menu (more than 8 chunks per
-// lane, or a single row larger than the LDS).
-constexpr int kHeldWaves = 4;
+// Held-row kernel geometry: 4 or 8 wavefronts, one workgroup per compute unit, each
+// holding up to as many rows as its LDS takes (the row's residual plus 12 bytes per
+// wavefront for the partial sums of squares and the per-token maxima). Rows are spread
+// evenly over the phases. Returns false when the row does not fit the kernel's menu (more
+// than 8 chunks per lane with 4 wavefronts or 4 with 8, or a single row larger than the
+// LDS).
 // LDS per workgroup assumed by arf_get_plan when the caller gives a CU count instead of
 // querying a device: gfx950's 160 KiB.
 constexpr int kPlanLdsBytes = 160 * 1024;
-bool held_plan(int64_t rows, int32_t hidden, const DeviceInfo& dev, int chunks, Plan* pl) {
+bool held_plan(int64_t rows, int32_t hidden, const DeviceInfo& dev, int waves, int chunks,
+               Plan* pl) {
     const int hc = hidden / 8;
-    if (chunks == 0) chunks = pow2_at_least(div_up(hc, kHeldWaves * 64));
-    if (chunks > 8 || kHeldWaves * 64 * chunks < hc) return false;
+    if (chunks == 0) chunks = pow2_at_least(div_up(hc, waves * 64));
+    if (chunks > (waves == 8 ? 4 : 8) || waves * 64 * chunks < hc) return false;
     // per held row: the residual plus each wavefront's sum of squares and maximum
-    const int64_t per_row = (int64_t)hidden * 2 + kHeldWaves * 12;
+    const int64_t per_row = (int64_t)hidden * 2 + waves * 12;
     const int64_t kmax = dev.lds / per_row;
     if (kmax < 1) return false;
     const int64_t grid = rows < dev.cus ? rows : dev.cus;
     const int64_t phases = div_up(rows, grid * kmax);
     const int64_t k = div_up(rows, grid * phases);
     pl->path = 3;
-    pl->waves = kHeldWaves;
+    pl->waves = waves;
     pl->chunks = chunks;
     pl->grid = (uint32_t)grid;
     pl->held = (int)k;
@@ -184,13 +185,23 @@ bool held_plan(int64_t rows, int32_t hidden, const DeviceInfo& dev, int chunks, 
 //    with at least 256 chunks take 4 counters and 4 workgroups per compute unit (8 x 16384
 //    x 4096: -6%; 16 x 16384 x 2048: -9% against one row per wavefront). Rows of 28 KiB
 //    and launches of 16 rows per compute unit gained nothing and keep their plans.
-bool held_wins(int64_t tokens, int32_t hidden, int n, int quant, const DeviceInfo& dev,
+// The held-row kernel with 8 wavefronts (half the chunks per lane, 2 wavefronts per SIMD)
+// exists for 16-bit partials, 1-4 shards and no quantised copy; there it measured 0.2-4.5%
+// faster than 4 wavefronts on every shape of the held region (2-4 bf16 shards, hidden
+// 4096-8192, 6-11 rows per CU; same outputs), and 1% slower for fp32 partials.
+bool held_eight(int pdt, int n, int quant, int32_t hidden) {
+    return pdt != ARF_F32 && n <= 4 && quant == arf::kQuantNone &&
+           pow2_at_least(div_up(hidden / 8, 8 * 64)) <= 4;
+}
+
+bool held_wins(int64_t tokens, int32_t hidden, int n, int quant, int pdt, const DeviceInfo& dev,
                Plan* pl) {
     if (n > 4 || hidden < 4096 || hidden > 8192 || quant != arf::kQuantNone ||
         tokens < 6LL * dev.cus || tokens > 16LL * dev.cus)
         return false;
     Plan h;
-    if (!held_plan(tokens, hidden, dev, 0, &h)) return false;
+    if (!held_plan(tokens, hidden, dev, held_eight(pdt, n, quant, hidden) ? 8 : 4, 0, &h))
+        return false;
     if ((int64_t)h.grid * h.held < tokens) return false;   // more than one batch
     *pl = h;
     return true;
@@ -226,8 +237,8 @@ ClaimRule forced_claim_rule(int64_t row_bytes) {
 constexpr int kStaticLdsSlack = 2048;
 
 // row_bytes: HBM traffic of one row (partials, residual, outputs), for the claim rule.
-arf_status make_plan(int64_t tokens, int32_t hidden, int n, int quant, int64_t row_bytes,
-                     const DeviceInfo& dev, bool reduce_only, Plan* pl) {
+arf_status make_plan(int64_t tokens, int32_t hidden, int n, int pdt, int quant,
+                     int64_t row_bytes, const DeviceInfo& dev, bool reduce_only, Plan* pl) {
     const int hc = hidden / 8;
     const int num_cus = dev.cus;
     int path = g_path.load(), waves = g_waves.load(), chunks = g_chunks.load();
@@ -237,11 +248,19 @@ arf_status make_plan(int64_t tokens, int32_t hidden, int n, int quant, int64_t r
     pl->claim_count = 0;
     pl->claim_split = 0;
     if (path == 3) {
-        // the held-row kernel has no reduce-only form: such calls take the default plan
-        if (!reduce_only) return held_plan(tokens, hidden, dev, chunks, pl) ? ARF_OK : ARF_ERR_VALUE;
+        // the held-row kernel has no reduce-only form: such calls take the default plan.
+        // Without a forced wave count, the plan's: 8 where that form exists and fits.
+        if (!reduce_only) {
+            const bool eight = held_eight(pdt, n, quant, hidden);
+            if (waves == 0 && eight && held_plan(tokens, hidden, dev, 8, chunks, pl)) return ARF_OK;
+            if (waves == 8 && !eight) return ARF_ERR_VALUE;
+            return held_plan(tokens, hidden, dev, waves ? waves : 4, chunks, pl) ? ARF_OK
+                                                                                : ARF_ERR_VALUE;
+        }
         path = waves = chunks = 0;
     }
-    if (path == 0 && !reduce_only && held_wins(tokens, hidden, n, quant, dev, pl)) return ARF_OK;
+    if (path == 0 && !reduce_only && held_wins(tokens, hidden, n, quant, pdt, dev, pl))
+        return ARF_OK;
     const bool forced_claims = path == 4;
     ClaimRule rule = forced_claims ? forced_claim_rule(row_bytes) : ClaimRule{0, 0};
     if (path == 0) {
@@ -304,12 +323,12 @@ arf_status make_plan(int64_t tokens, int32_t hidden, int n, int quant, int64_t r
     return ARF_OK;
 }
 
-held_launch_fn lookup_held(int pdt, int adt, int n, int c, bool quant) {
+held_launch_fn lookup_held(int pdt, int adt, int n, int c, bool quant, int waves) {
 #define ARF_BY_RANGE(PD, AD)                                                 \
-    if (n <= 4) return arf::held_##PD##_##AD##_n01_04(n, c, quant);          \
-    if (n <= 8) return arf::held_##PD##_##AD##_n05_08(n, c, quant);          \
-    if (n <= 12) return arf::held_##PD##_##AD##_n09_12(n, c, quant);         \
-    return arf::held_##PD##_##AD##_n13_16(n, c, quant);
+    if (n <= 4) return arf::held_##PD##_##AD##_n01_04(n, c, quant, waves);   \
+    if (n <= 8) return arf::held_##PD##_##AD##_n05_08(n, c, quant, waves);   \
+    if (n <= 12) return arf::held_##PD##_##AD##_n09_12(n, c, quant, waves);  \
+    return arf::held_##PD##_##AD##_n13_16(n, c, quant, waves);
     if (adt == ARF_BF16) {
         if (pdt == ARF_F32) { ARF_BY_RANGE(f32, bf16) }
         ARF_BY_RANGE(bf16, bf16)
@@ -474,8 +493,8 @@ arf_status run(Call c, void* stream) {
                                                         : 0;
     const int64_t row_bytes = (int64_t)c.n * c.hidden * sp + 2LL * c.hidden * 3 + qbytes;
     Plan pl;
-    if ((st = make_plan(c.row_count, c.hidden, c.n, c.quant, row_bytes, dev, c.reduce_only,
-                        &pl)) != ARF_OK)
+    if ((st = make_plan(c.row_count, c.hidden, c.n, c.pdt, c.quant, row_bytes, dev,
+                        c.reduce_only, &pl)) != ARF_OK)
         return st;
     uint32_t* counter = pl.path == 4 ? claim_counter(dev.index, stream) : nullptr;
     if (pl.path == 4 && !counter) {   // the same kernel with rows by workgroup index
@@ -485,7 +504,8 @@ arf_status run(Call c, void* stream) {
     }
     launch_fn fn = nullptr;
     held_launch_fn hfn = nullptr;
-    if (pl.path == 3) hfn = lookup_held(c.pdt, c.adt, c.n, pl.chunks, c.quant != arf::kQuantNone);
+    if (pl.path == 3)
+        hfn = lookup_held(c.pdt, c.adt, c.n, pl.chunks, c.quant != arf::kQuantNone, pl.waves);
     else fn = lookup(c.pdt, c.adt, c.n, pl);
     if (!fn && !hfn) return ARF_ERR_VALUE;
     arf::Params p;
@@ -714,7 +734,8 @@ arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
     const int64_t row_bytes = (int64_t)n_shards * hidden * (partial_dtype == ARF_F32 ? 4 : 2) +
                               2LL * hidden * 3;
     Plan pl;
-    arf_status st = make_plan(tokens, hidden, n_shards, arf::kQuantNone, row_bytes, dev, false, &pl);
+    arf_status st = make_plan(tokens, hidden, n_shards, partial_dtype, arf::kQuantNone, row_bytes,
+                              dev, false, &pl);
     if (st != ARF_OK) return st;
     out[0] = pl.path;
     out[1] = pl.waves;
@@ -727,12 +748,14 @@ arf_status arf_set_path_override(int32_t path, int32_t waves_per_block,
                                  int32_t chunks_per_lane) {
     if (path < 0 || path > 4) return ARF_ERR_VALUE;
     if (path == 0 && (waves_per_block || chunks_per_lane)) return ARF_ERR_VALUE;
-    if ((path == 1 || path == 3) && waves_per_block && waves_per_block != 4) return ARF_ERR_VALUE;
+    if (path == 1 && waves_per_block && waves_per_block != 4) return ARF_ERR_VALUE;
+    if (path == 3 && waves_per_block && waves_per_block != 4 && waves_per_block != 8)
+        return ARF_ERR_VALUE;
     if ((path == 2 || path == 4) && waves_per_block && !in_menu_w(waves_per_block))
         return ARF_ERR_VALUE;
     if (chunks_per_lane && !in_menu_c(chunks_per_lane)) return ARF_ERR_VALUE;
     g_path.store(path);
-    g_waves.store(path == 2 || path == 4 ? waves_per_block : 0);   // paths 1 and 3 use 4
+    g_waves.store(path >= 2 ? waves_per_block : 0);   // path 1 uses 4
     g_chunks.store(chunks_per_lane);
     return ARF_OK;
 }

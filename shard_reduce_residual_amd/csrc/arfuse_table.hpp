@@ -69,34 +69,38 @@ launch_fn pick_shards(int n, bool row_per_wave, int waves, int c) {
     }
 }
 
-// Held-row kernel: 4 wavefronts (one per SIMD, so each may use the whole register file),
-// chunks per lane in {1, 2, 4, 8}: rows of up to 16384 elements. Every shard count has the
-// general form (any quantised copy); the shard counts the plan sends to held rows (1..4)
-// also have the form without a quantised copy, which those calls take.
-template <class PT, class AT, int N, bool QUANT>
+// Held-row kernels: 4 wavefronts with C in {1, 2, 4, 8}, in the form without a quantised
+// copy for the shard counts the plan sends to held rows (1..4) and in the general form (any
+// quantised copy) for all; and 8 wavefronts with C in {1, 2, 4} for 16-bit partials without
+// a quantised copy (1..4 shards), the plan's choice for them (2 wavefronts per SIMD).
+template <class PT, class AT, int N, int W, bool QUANT>
 held_launch_fn pick_held_c(int c) {
     switch (c) {
-        case 1: return &launch_held<PT, AT, N, 1, 4, QUANT>;
-        case 2: return &launch_held<PT, AT, N, 2, 4, QUANT>;
-        case 4: return &launch_held<PT, AT, N, 4, 4, QUANT>;
-        case 8: return &launch_held<PT, AT, N, 8, 4, QUANT>;
+        case 1: return &launch_held<PT, AT, N, 1, W, QUANT>;
+        case 2: return &launch_held<PT, AT, N, 2, W, QUANT>;
+        case 4: return &launch_held<PT, AT, N, 4, W, QUANT>;
+        case 8: if constexpr (W == 4) return &launch_held<PT, AT, N, 8, W, QUANT>;
+                return nullptr;
         default: return nullptr;
     }
 }
 
 template <class PT, class AT, int N>
-held_launch_fn pick_held(int c, bool quant) {
+held_launch_fn pick_held(int c, bool quant, int waves) {
     if constexpr (N <= 4) {
-        if (!quant) return pick_held_c<PT, AT, N, false>(c);
+        if (!quant && waves == 4) return pick_held_c<PT, AT, N, 4, false>(c);
+        if constexpr (PartTraits<PT>::kPieces == 1) {
+            if (!quant && waves == 8) return pick_held_c<PT, AT, N, 8, false>(c);
+        }
     }
-    return pick_held_c<PT, AT, N, true>(c);
+    return waves == 4 ? pick_held_c<PT, AT, N, 4, true>(c) : nullptr;
 }
 
 template <class PT, class AT, int NLO, int NHI>
-held_launch_fn pick_held_shards(int n, int c, bool quant) {
+held_launch_fn pick_held_shards(int n, int c, bool quant, int waves) {
     if constexpr (NLO <= NHI) {
-        if (n == NLO) return pick_held<PT, AT, NLO>(c, quant);
-        return pick_held_shards<PT, AT, NLO + 1, NHI>(n, c, quant);
+        if (n == NLO) return pick_held<PT, AT, NLO>(c, quant, waves);
+        return pick_held_shards<PT, AT, NLO + 1, NHI>(n, c, quant, waves);
     } else {
         return nullptr;
     }
@@ -108,10 +112,10 @@ held_launch_fn pick_held_shards(int n, int c, bool quant) {
     launch_fn lookup_##PD##_##AD##_n05_08(int n, bool rpw, int waves, int c);    \
     launch_fn lookup_##PD##_##AD##_n09_12(int n, bool rpw, int waves, int c);    \
     launch_fn lookup_##PD##_##AD##_n13_16(int n, bool rpw, int waves, int c);    \
-    held_launch_fn held_##PD##_##AD##_n01_04(int n, int c, bool quant);                      \
-    held_launch_fn held_##PD##_##AD##_n05_08(int n, int c, bool quant);                      \
-    held_launch_fn held_##PD##_##AD##_n09_12(int n, int c, bool quant);                      \
-    held_launch_fn held_##PD##_##AD##_n13_16(int n, int c, bool quant);
+    held_launch_fn held_##PD##_##AD##_n01_04(int n, int c, bool quant, int waves);           \
+    held_launch_fn held_##PD##_##AD##_n05_08(int n, int c, bool quant, int waves);           \
+    held_launch_fn held_##PD##_##AD##_n09_12(int n, int c, bool quant, int waves);           \
+    held_launch_fn held_##PD##_##AD##_n13_16(int n, int c, bool quant, int waves);
 ARF_DECLARE_LOOKUPS(bf16, bf16)
 ARF_DECLARE_LOOKUPS(f16, f16)
 ARF_DECLARE_LOOKUPS(f32, bf16)

@@ -5,7 +5,7 @@ namespace arf {
 launch_fn lookup_f32_bf16_n01_04(int n, bool rpw, int waves, int c) {
     return pick_shards<PartF32, ActBF16, 1, 4>(n, rpw, waves, c);
 }
-held_launch_fn held_f32_bf16_n01_04(int n, int c, bool quant) {
-    return pick_held_shards<PartF32, ActBF16, 1, 4>(n, c, quant);
+held_launch_fn held_f32_bf16_n01_04(int n, int c, bool quant, int waves) {
+    return pick_held_shards<PartF32, ActBF16, 1, 4>(n, c, quant, waves);
 }
 }  // namespace arf

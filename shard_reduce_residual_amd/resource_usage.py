@@ -103,8 +103,8 @@ def report(cus: int = 256) -> str:
         pt, at = "arf::" + TAG[w.partial_dtype], "arf::" + TAG[w.act_dtype]
         if plan["path"] == 3:
             # the plan's held calls have no quantised copy: the QUANT = false form
-            name = "void arf::fused_held_rows<%s, %s, %d, %d, 4, false>(arf::Params)" % (
-                pt, at, w.n_shards, plan["chunks"])
+            name = "void arf::fused_held_rows<%s, %s, %d, %d, %d, false>(arf::Params)" % (
+                pt, at, w.n_shards, plan["chunks"], plan["waves"])
             rows = -(-w.tokens // plan["grid"])
             dyn = rows * (2 * w.hidden + 12 * plan["waves"])
         else:

@@ -13,7 +13,7 @@
 namespace arf {
 #define ARF_STUB(PD, AD, R)                                                         \
     launch_fn lookup_##PD##_##AD##_##R(int, bool, int, int) { return nullptr; }     \
-    held_launch_fn held_##PD##_##AD##_##R(int, int, bool) { return nullptr; }
+    held_launch_fn held_##PD##_##AD##_##R(int, int, bool, int) { return nullptr; }
 #define ARF_STUBS(PD, AD) \
     ARF_STUB(PD, AD, n01_04) ARF_STUB(PD, AD, n05_08) ARF_STUB(PD, AD, n09_12) ARF_STUB(PD, AD, n13_16)
 ARF_STUBS(bf16, bf16)
@@ -132,7 +132,9 @@ int main() {
                     const int64_t lanes = o[0] == 1 ? 64 : 64 * (int64_t)o[1];
                     EXPECT(o[0] == 1 || o[0] == 2 || (o[0] == 3 && n <= 4) || o[0] == 4);
                     EXPECT(o[2] == 1 || o[2] == 2 || o[2] == 4 || o[2] == 8);
-                    EXPECT(o[0] == 2 ? (o[1] == 4 || o[1] == 8 || o[1] == 16) : o[1] == 4);
+                    EXPECT(o[0] == 2 ? (o[1] == 4 || o[1] == 8 || o[1] == 16)
+                                     : o[0] == 3 ? (o[1] == 4 || (o[1] == 8 && n <= 4 && o[2] <= 4))
+                                                 : o[1] == 4);
                     EXPECT(lanes * o[2] * 8 >= h);
                     // held rows: one workgroup per compute unit, the whole launch in one batch
                     // of at most 160 KiB of LDS per workgroup; claimed rows: a static prefix
@@ -162,7 +164,7 @@ int main() {
                     if (o[0] != 2 && o[0] != 1) EXPECT((int64_t)(uint32_t)o[3] * lanes <= (int64_t)UINT32_MAX);
                     if (o[0] == 3) {
                         EXPECT(t >= 6LL * cus && t <= 16LL * cus && h >= 4096 && h <= 8192);
-                        EXPECT(div_up_i64(t, cus) * (2LL * h + 48) <= 160 * 1024);
+                        EXPECT(div_up_i64(t, cus) * (2LL * h + 12LL * o[1]) <= 160 * 1024);
                     }
                 }
             }
@@ -203,7 +205,7 @@ int main() {
     EXPECT(arf_set_path_override(4, 16, 8) == ARF_OK);
     EXPECT(arf_get_plan(3, 100, 65536, ARF_BF16, 256, o) == ARF_OK && o[0] == 4 && o[1] == 16 && o[2] == 8);
     EXPECT(arf_get_plan(3, 100, 65544, ARF_BF16, 256, o) == ARF_ERR_SHAPE);
-    const int bad[][3] = {{5, 0, 0}, {-1, 0, 0}, {0, 4, 0}, {0, 0, 2}, {1, 8, 0}, {2, 3, 0}, {2, 4, 3}, {2, 32, 1}, {3, 8, 0}, {3, 0, 3}, {4, 2, 0}, {4, 0, 3}};
+    const int bad[][3] = {{5, 0, 0}, {-1, 0, 0}, {0, 4, 0}, {0, 0, 2}, {1, 8, 0}, {2, 3, 0}, {2, 4, 3}, {2, 32, 1}, {3, 16, 0}, {3, 0, 3}, {4, 2, 0}, {4, 0, 3}};
     for (const auto& v : bad) EXPECT(arf_set_path_override(v[0], v[1], v[2]) == ARF_ERR_VALUE);
     EXPECT(arf_set_path_override(0, 0, 0) == ARF_OK);
     EXPECT(arf_get_plan(8, 8192, 16384, ARF_BF16, 256, o) == ARF_OK && o[0] == 4 && o[1] == 4 && o[2] == 8 && o[3] == 8704);

@@ -145,8 +145,9 @@ def test_plan_covers_the_row_and_follows_the_menu():
                         # rounded up to a multiple of 8 * split (split 2 or 4)
                         assert p["waves"] == 4 and t >= 8 * 256
                         assert 0 <= p["grid"] - (t + max(64, t // 16)) < 32
-                    else:   # held rows: one workgroup per CU, one batch of rows each
-                        assert p["path"] == 3 and n <= 4 and p["waves"] == 4
+                    else:   # held rows: one workgroup per CU, one batch of rows each;
+                        # 8 wavefronts for 16-bit partials (these are bf16)
+                        assert p["path"] == 3 and n <= 4 and p["waves"] == 8
                         assert p["grid"] == min(t, 256) and 6 * 256 <= t <= 16 * 256
     finally:
         arf.arf_set_path_override(0)
@@ -250,7 +251,7 @@ def test_path_override_forces_and_rejects():
         assert plan(8, 8192, 1024)["path"] == 4
         arf.arf_set_path_override(4, 8, 0)
         assert plan(8, 3, 16384) == {"path": 4, "waves": 8, "chunks": 4, "grid": 72}
-        for bad in ((5, 0, 0), (0, 4, 0), (2, 3, 0), (2, 2, 0), (2, 4, 3), (1, 8, 0), (3, 8, 0),
+        for bad in ((5, 0, 0), (0, 4, 0), (2, 3, 0), (2, 2, 0), (2, 4, 3), (1, 8, 0), (3, 16, 0),
                     (4, 2, 0), (4, 4, 3)):
             with pytest.raises(arf.ArfError):
                 arf.arf_set_path_override(*bad)

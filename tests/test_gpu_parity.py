@@ -917,6 +917,29 @@ def test_split_claim_plans_every_row(shape):
         compare(got, ref, "%s, call %d" % (shape, k))
 
 
+@pytest.mark.parametrize("shape", [(2, 2048, 7168, "bf16"), (4, 4096, 4096, "f16"),
+                                   (3, 1536, 8192, "bf16")])
+def test_held_rows_with_eight_wavefronts_every_row(shape):
+    # 16-bit partials in the held-row region: the plan takes the held kernel with 8
+    # wavefronts (half the chunks per lane); every row against the oracle, then the same
+    # call with 4 wavefronts forced, which must give the same outputs within the tolerance
+    n, t, h, dt = shape
+    w = _case(n, t, h, dt, dt, 615, quant=None)
+    plan = arf.arf_get_plan(n, t, h, {"bf16": 0, "f16": 1}[dt])
+    assert plan["path"] == 3 and plan["waves"] == 8, plan
+    say("held rows, 8 wavefronts, %s" % (shape,))
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    ref = run_oracle(p, r, g, w.eps, dt, dt)
+    compare(run_gpu(pd_, rd, gd, w.eps, dt), ref, "%s, 8 wavefronts" % (shape,))
+    try:
+        arf.arf_set_path_override(3, 4, 0)
+        assert arf.arf_get_plan(n, t, h, {"bf16": 0, "f16": 1}[dt])["waves"] == 4
+        got4 = run_gpu(pd_, rd, gd, w.eps, dt)
+    finally:
+        arf.arf_set_path_override(0)
+    compare(got4, ref, "%s, 4 wavefronts" % (shape,))
+
+
 # ---- HIP graph capture --------------------------------------------------------------------
 
 @pytest.mark.parametrize("path", [0, 4])
