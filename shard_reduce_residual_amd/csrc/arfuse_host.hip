@@ -161,8 +161,9 @@ bool held_plan(int64_t rows, int32_t hidden, const DeviceInfo& dev, int waves, i
 //      compute unit;
 //    - rows too wide for 8 chunks per lane use 16 wavefronts.
 //  * held rows (path 3) where that measured faster (sweep of 175 shapes, bit-identical
-//    outputs): at most 4 shards, 4096 <= hidden <= 8192, no quantised copy, 6 to 16 rows
-//    per compute unit and no more than one batch per workgroup holds. There HBM sees the whole
+//    outputs, and 40 more with 5-16 shards, see held_eight): 4096 <= hidden <= 8192, no
+//    quantised copy, 6 to 16 rows per compute unit, no more than one batch per workgroup
+//    holds, and at most 4 shards for fp32 partials (any count for 16-bit ones). There HBM sees the whole
 //    launch's reads, then its writes: 2-10% faster (3% for 4 fp32 shards of 2048 x 7168). With more shards, other
 //    row sizes, several batches, or the per-token scale's extra pass over the held rows, it
 //    was slower than one row per workgroup.
@@ -186,22 +187,26 @@ bool held_plan(int64_t rows, int32_t hidden, const DeviceInfo& dev, int waves, i
 //    x 4096: -6%; 16 x 16384 x 2048: -9% against one row per wavefront). Rows of 28 KiB
 //    and launches of 16 rows per compute unit gained nothing and keep their plans.
 // The held-row kernel with 8 wavefronts (half the chunks per lane, 2 wavefronts per SIMD)
-// exists for 16-bit partials, 1-4 shards and no quantised copy; there it measured 0.2-4.5%
-// faster than 4 wavefronts on every shape of the held region (2-4 bf16 shards, hidden
-// 4096-8192, 6-11 rows per CU; same outputs), and 1% slower for fp32 partials.
-bool held_eight(int pdt, int n, int quant, int32_t hidden) {
-    return pdt != ARF_F32 && n <= 4 && quant == arf::kQuantNone &&
+// exists for 16-bit partials without a quantised copy, for every shard count. With 1-4
+// shards it measured -7% to +1.6% against 4 wavefronts over the held region (better on
+// balance), and 1% slower for fp32 partials. With 5-16 shards it opens the held region to
+// them: against the plan's rows by index or claims it was 2-12% faster on 38 of 40 shapes
+// (5, 6, 8, 12, 16 shards, hidden 4096-8192, 6-16 rows per CU; 16 x 3072 x 4096: 83.9 ->
+// 73.6 us), level on 8 x 1536 x 4096 and 3% slower on 16 x 2048 x 8192.
+bool held_eight(int pdt, int quant, int32_t hidden) {
+    return pdt != ARF_F32 && quant == arf::kQuantNone &&
            pow2_at_least(div_up(hidden / 8, 8 * 64)) <= 4;
 }
 
 bool held_wins(int64_t tokens, int32_t hidden, int n, int quant, int pdt, const DeviceInfo& dev,
                Plan* pl) {
-    if (n > 4 || hidden < 4096 || hidden > 8192 || quant != arf::kQuantNone ||
+    if (hidden < 4096 || hidden > 8192 || quant != arf::kQuantNone ||
         tokens < 6LL * dev.cus || tokens > 16LL * dev.cus)
         return false;
+    const bool eight = held_eight(pdt, quant, hidden);
+    if (n > 4 && !eight) return false;   // fp32 partials: held rows up to 4 shards
     Plan h;
-    if (!held_plan(tokens, hidden, dev, held_eight(pdt, n, quant, hidden) ? 8 : 4, 0, &h))
-        return false;
+    if (!held_plan(tokens, hidden, dev, eight ? 8 : 4, 0, &h)) return false;
     if ((int64_t)h.grid * h.held < tokens) return false;   // more than one batch
     *pl = h;
     return true;
@@ -251,7 +256,7 @@ arf_status make_plan(int64_t tokens, int32_t hidden, int n, int pdt, int quant,
         // the held-row kernel has no reduce-only form: such calls take the default plan.
         // Without a forced wave count, the plan's: 8 where that form exists and fits.
         if (!reduce_only) {
-            const bool eight = held_eight(pdt, n, quant, hidden);
+            const bool eight = held_eight(pdt, quant, hidden);
             if (waves == 0 && eight && held_plan(tokens, hidden, dev, 8, chunks, pl)) return ARF_OK;
             if (waves == 8 && !eight) return ARF_ERR_VALUE;
             return held_plan(tokens, hidden, dev, waves ? waves : 4, chunks, pl) ? ARF_OK

@@ -70,9 +70,9 @@ launch_fn pick_shards(int n, bool row_per_wave, int waves, int c) {
 }
 
 // Held-row kernels: 4 wavefronts with C in {1, 2, 4, 8}, in the form without a quantised
-// copy for the shard counts the plan sends to held rows (1..4) and in the general form (any
-// quantised copy) for all; and 8 wavefronts with C in {1, 2, 4} for 16-bit partials without
-// a quantised copy (1..4 shards), the plan's choice for them (2 wavefronts per SIMD).
+// copy for 1..4 shards and in the general form (any quantised copy) for all; and 8
+// wavefronts with C in {1, 2, 4} for 16-bit partials without a quantised copy (all shard
+// counts), the plan's choice for them (2 wavefronts per SIMD).
 template <class PT, class AT, int N, int W, bool QUANT>
 held_launch_fn pick_held_c(int c) {
     switch (c) {
@@ -89,9 +89,9 @@ template <class PT, class AT, int N>
 held_launch_fn pick_held(int c, bool quant, int waves) {
     if constexpr (N <= 4) {
         if (!quant && waves == 4) return pick_held_c<PT, AT, N, 4, false>(c);
-        if constexpr (PartTraits<PT>::kPieces == 1) {
-            if (!quant && waves == 8) return pick_held_c<PT, AT, N, 8, false>(c);
-        }
+    }
+    if constexpr (PartTraits<PT>::kPieces == 1) {
+        if (!quant && waves == 8) return pick_held_c<PT, AT, N, 8, false>(c);
     }
     return waves == 4 ? pick_held_c<PT, AT, N, 4, true>(c) : nullptr;
 }

@@ -130,10 +130,10 @@ int main() {
                     int32_t o[4];
                     if (arf_get_plan(n, t, h, ARF_BF16, cus, o) != ARF_OK) { EXPECT(false); continue; }
                     const int64_t lanes = o[0] == 1 ? 64 : 64 * (int64_t)o[1];
-                    EXPECT(o[0] == 1 || o[0] == 2 || (o[0] == 3 && n <= 4) || o[0] == 4);
+                    EXPECT(o[0] == 1 || o[0] == 2 || o[0] == 3 || o[0] == 4);
                     EXPECT(o[2] == 1 || o[2] == 2 || o[2] == 4 || o[2] == 8);
                     EXPECT(o[0] == 2 ? (o[1] == 4 || o[1] == 8 || o[1] == 16)
-                                     : o[0] == 3 ? (o[1] == 4 || (o[1] == 8 && n <= 4 && o[2] <= 4))
+                                     : o[0] == 3 ? (o[1] == 8 && o[2] <= 4)   // bf16: 8 wavefronts
                                                  : o[1] == 4);
                     EXPECT(lanes * o[2] * 8 >= h);
                     // held rows: one workgroup per compute unit, the whole launch in one batch
@@ -181,10 +181,11 @@ int main() {
     EXPECT(arf_get_plan(3, 100, 65536, ARF_BF16, 256, o) == ARF_OK && o[1] == 16 && o[2] == 8);
     EXPECT(arf_set_path_override(2, 4, 1) == ARF_OK);
     EXPECT(arf_get_plan(3, 100, 4096, ARF_BF16, 256, o) == ARF_ERR_VALUE);
-    // held rows forced: 4 wavefronts, grid min(rows, CUs); refused where a row needs more
-    // than 8 chunks per lane
+    // held rows forced: 8 wavefronts for 16-bit partials (4 for fp32), grid min(rows,
+    // CUs); refused where a row needs more than 8 chunks per lane
     EXPECT(arf_set_path_override(3, 0, 0) == ARF_OK);
-    EXPECT(arf_get_plan(8, 100, 16384, ARF_BF16, 256, o) == ARF_OK && o[0] == 3 && o[1] == 4 && o[2] == 8 && o[3] == 100);
+    EXPECT(arf_get_plan(8, 100, 16384, ARF_BF16, 256, o) == ARF_OK && o[0] == 3 && o[1] == 8 && o[2] == 4 && o[3] == 100);
+    EXPECT(arf_get_plan(8, 100, 16384, ARF_F32, 256, o) == ARF_OK && o[0] == 3 && o[1] == 4 && o[2] == 8 && o[3] == 100);
     EXPECT(arf_get_plan(8, 8192, 1024, ARF_BF16, 256, o) == ARF_OK && o[0] == 3 && o[2] == 1 && o[3] == 256);
     EXPECT(arf_get_plan(8, 100, 16392, ARF_BF16, 256, o) == ARF_ERR_VALUE);
     EXPECT(arf_set_path_override(3, 4, 2) == ARF_OK);
@@ -220,7 +221,8 @@ int main() {
     EXPECT(arf_get_plan(4, 8192, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 4 && o[3] == 8704);
     // held rows by default only in their measured range
     EXPECT(arf_get_plan(4, 2048, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 3 && o[2] == 4 && o[3] == 256);
-    EXPECT(arf_get_plan(8, 2048, 7168, ARF_BF16, 256, o) == ARF_OK && o[0] == 2);
+    EXPECT(arf_get_plan(8, 2048, 7168, ARF_BF16, 256, o) == ARF_OK && o[0] == 3 && o[1] == 8);
+    EXPECT(arf_get_plan(8, 2048, 7168, ARF_F32, 256, o) == ARF_OK && o[0] != 3);
     EXPECT(arf_get_plan(4, 1535, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 2);
     EXPECT(arf_get_plan(4, 1536, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 3);
     EXPECT(arf_get_plan(4, 4096, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 4);   // two batches: claimed rows

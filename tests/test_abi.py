@@ -147,7 +147,7 @@ def test_plan_covers_the_row_and_follows_the_menu():
                         assert 0 <= p["grid"] - (t + max(64, t // 16)) < 32
                     else:   # held rows: one workgroup per CU, one batch of rows each;
                         # 8 wavefronts for 16-bit partials (these are bf16)
-                        assert p["path"] == 3 and n <= 4 and p["waves"] == 8
+                        assert p["path"] == 3 and p["waves"] == 8
                         assert p["grid"] == min(t, 256) and 6 * 256 <= t <= 16 * 256
     finally:
         arf.arf_set_path_override(0)
@@ -188,8 +188,8 @@ def test_plan_row_per_wave_region():
     assert plan(16, 16384, 1024)["path"] == 1           # 128 chunks: no claims
     assert plan(4, 8191, 2056, 2)["path"] == 2          # 257 chunks
     assert plan(4, 8192, 2056, 2)["path"] == 4          # 257 chunks, claimed from 32 per CU
-    for t in (512, 1024, 2048, 4096, 8191):
-        assert plan(8, t, 4096)["path"] == 2
+    for t in (512, 1024, 2048, 4096, 8191):   # never one row per wavefront (held rows at
+        assert plan(8, t, 4096)["path"] != 1      # 6-16 rows per CU)
     # the thresholds scale with the CU count
     assert plan(8, 1023, 2048, 0, 128)["path"] == 2 and plan(8, 1024, 2048, 0, 128)["path"] == 1
 
@@ -201,7 +201,8 @@ def test_plan_held_rows_region():
     assert plan(4, 11 * 256, 7168, 2)["path"] == 3 and plan(4, 11 * 256 + 1, 7168, 2)["path"] == 2
     assert plan(2, 9 * 256, 8192)["path"] == 3 and plan(2, 9 * 256 + 1, 8192)["path"] == 2
     assert plan(4, 16 * 256, 4096)["path"] == 3 and plan(4, 16 * 256 + 1, 4096)["path"] == 2
-    assert plan(5, 2048, 7168)["path"] == 2
+    assert plan(5, 2048, 7168) == {"path": 3, "waves": 8, "chunks": 2, "grid": 256}
+    assert plan(16, 4096, 4096)["path"] == 3 and plan(5, 2048, 7168, 2)["path"] != 3
     assert plan(4, 2048, 4088)["path"] != 3 and plan(4, 2048, 4096)["path"] == 3
     assert plan(4, 2048, 8200)["path"] == 2
     # the thresholds scale with the CU count
@@ -240,7 +241,12 @@ def test_path_override_forces_and_rejects():
         with pytest.raises(arf.ArfError):
             plan(8, 8, 16384)
         arf.arf_set_path_override(3)
+        # held rows without a wave count: 8 wavefronts for 16-bit partials, else 4
+        assert plan(8, 8192, 16384) == {"path": 3, "waves": 8, "chunks": 4, "grid": 256}
+        assert plan(8, 8192, 16384, 2) == {"path": 3, "waves": 4, "chunks": 8, "grid": 256}
+        arf.arf_set_path_override(3, 4, 0)
         assert plan(8, 8192, 16384) == {"path": 3, "waves": 4, "chunks": 8, "grid": 256}
+        arf.arf_set_path_override(3)
         with pytest.raises(arf.ArfError):
             plan(8, 8, 16392)            # more than 8 chunks per lane
         arf.arf_set_path_override(3, 4, 4)

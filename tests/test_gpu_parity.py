@@ -918,11 +918,13 @@ def test_split_claim_plans_every_row(shape):
 
 
 @pytest.mark.parametrize("shape", [(2, 2048, 7168, "bf16"), (4, 4096, 4096, "f16"),
-                                   (3, 1536, 8192, "bf16")])
+                                   (3, 1536, 8192, "bf16"), (8, 2048, 7168, "bf16"),
+                                   (16, 1536, 4096, "f16")])
 def test_held_rows_with_eight_wavefronts_every_row(shape):
-    # 16-bit partials in the held-row region: the plan takes the held kernel with 8
-    # wavefronts (half the chunks per lane); every row against the oracle, then the same
-    # call with 4 wavefronts forced, which must give the same outputs within the tolerance
+    # 16-bit partials in the held-row region (any shard count): the plan takes the held
+    # kernel with 8 wavefronts (half the chunks per lane); every row against the oracle,
+    # then the same call with 4 wavefronts forced (the general form beyond 4 shards), which
+    # must give the same outputs within the tolerance
     n, t, h, dt = shape
     w = _case(n, t, h, dt, dt, 615, quant=None)
     plan = arf.arf_get_plan(n, t, h, {"bf16": 0, "f16": 1}[dt])
