@@ -163,7 +163,7 @@ bool held_plan(int64_t rows, int32_t hidden, const DeviceInfo& dev, int waves, i
 //  * held rows (path 3) where that measured faster (sweep of 175 shapes, bit-identical
 //    outputs, and 40 more with 5-16 shards, see held_eight): 4096 <= hidden <= 8192, no
 //    quantised copy, 6 to 16 rows per compute unit, no more than one batch per workgroup
-//    holds, and at most 4 shards for fp32 partials (any count for 16-bit ones). There HBM sees the whole
+//    holds; for fp32 partials beyond 4 shards, shards x chunks per lane <= 48. There HBM sees the whole
 //    launch's reads, then its writes: 2-10% faster (3% for 4 fp32 shards of 2048 x 7168). With more shards, other
 //    row sizes, several batches, or the per-token scale's extra pass over the held rows, it
 //    was slower than one row per workgroup.
@@ -204,9 +204,13 @@ bool held_wins(int64_t tokens, int32_t hidden, int n, int quant, int pdt, const 
         tokens < 6LL * dev.cus || tokens > 16LL * dev.cus)
         return false;
     const bool eight = held_eight(pdt, quant, hidden);
-    if (n > 4 && !eight) return false;   // fp32 partials: held rows up to 4 shards
     Plan h;
     if (!held_plan(tokens, hidden, dev, eight ? 8 : 4, 0, &h)) return false;
+    // fp32 partials beyond 4 shards: the 4-wavefront form without a quantised copy, where
+    // shards x chunks per lane <= 48 (5-16 shards, 6-16 rows per CU: 0.5-10% faster than
+    // rows by index or claims on 34 of 40 shapes; 16 shards x 4 chunks ran out of
+    // registers, 16-23% slower)
+    if (!eight && n > 4 && (h.chunks > 4 || n * h.chunks > 48)) return false;
     if ((int64_t)h.grid * h.held < tokens) return false;   // more than one batch
     *pl = h;
     return true;

@@ -69,17 +69,19 @@ launch_fn pick_shards(int n, bool row_per_wave, int waves, int c) {
     }
 }
 
-// Held-row kernels: 4 wavefronts with C in {1, 2, 4, 8}, in the form without a quantised
-// copy for 1..4 shards and in the general form (any quantised copy) for all; and 8
-// wavefronts with C in {1, 2, 4} for 16-bit partials without a quantised copy (all shard
-// counts), the plan's choice for them (2 wavefronts per SIMD).
-template <class PT, class AT, int N, int W, bool QUANT>
+// Held-row kernels: 4 wavefronts with C in {1, 2, 4, 8}, in the general form (any quantised
+// copy) for all shard counts and in the form without a quantised copy for 1..4 shards
+// (and for fp32 partials with C in {1, 2, 4}, all shard counts); and 8 wavefronts with C in
+// {1, 2, 4} for 16-bit partials without a quantised copy (all shard counts). The plan
+// takes the forms without a quantised copy: 8 wavefronts (2 per SIMD) for 16-bit partials,
+// 4 for fp32 ones.
+template <class PT, class AT, int N, int W, bool QUANT, int CMAX>
 held_launch_fn pick_held_c(int c) {
     switch (c) {
         case 1: return &launch_held<PT, AT, N, 1, W, QUANT>;
         case 2: return &launch_held<PT, AT, N, 2, W, QUANT>;
         case 4: return &launch_held<PT, AT, N, 4, W, QUANT>;
-        case 8: if constexpr (W == 4) return &launch_held<PT, AT, N, 8, W, QUANT>;
+        case 8: if constexpr (CMAX >= 8) return &launch_held<PT, AT, N, 8, W, QUANT>;
                 return nullptr;
         default: return nullptr;
     }
@@ -88,12 +90,14 @@ held_launch_fn pick_held_c(int c) {
 template <class PT, class AT, int N>
 held_launch_fn pick_held(int c, bool quant, int waves) {
     if constexpr (N <= 4) {
-        if (!quant && waves == 4) return pick_held_c<PT, AT, N, 4, false>(c);
+        if (!quant && waves == 4) return pick_held_c<PT, AT, N, 4, false, 8>(c);
+    } else if constexpr (PartTraits<PT>::kPieces == 2) {
+        if (!quant && waves == 4 && c <= 4) return pick_held_c<PT, AT, N, 4, false, 4>(c);
     }
     if constexpr (PartTraits<PT>::kPieces == 1) {
-        if (!quant && waves == 8) return pick_held_c<PT, AT, N, 8, false>(c);
+        if (!quant && waves == 8) return pick_held_c<PT, AT, N, 8, false, 4>(c);
     }
-    return waves == 4 ? pick_held_c<PT, AT, N, 4, true>(c) : nullptr;
+    return waves == 4 ? pick_held_c<PT, AT, N, 4, true, 8>(c) : nullptr;
 }
 
 template <class PT, class AT, int NLO, int NHI>

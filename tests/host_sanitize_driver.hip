@@ -222,7 +222,8 @@ int main() {
     // held rows by default only in their measured range
     EXPECT(arf_get_plan(4, 2048, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 3 && o[2] == 4 && o[3] == 256);
     EXPECT(arf_get_plan(8, 2048, 7168, ARF_BF16, 256, o) == ARF_OK && o[0] == 3 && o[1] == 8);
-    EXPECT(arf_get_plan(8, 2048, 7168, ARF_F32, 256, o) == ARF_OK && o[0] != 3);
+    EXPECT(arf_get_plan(8, 2048, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 3 && o[1] == 4);
+    EXPECT(arf_get_plan(16, 2048, 7168, ARF_F32, 256, o) == ARF_OK && o[0] != 3);
     EXPECT(arf_get_plan(4, 1535, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 2);
     EXPECT(arf_get_plan(4, 1536, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 3);
     EXPECT(arf_get_plan(4, 4096, 7168, ARF_F32, 256, o) == ARF_OK && o[0] == 4);   // two batches: claimed rows

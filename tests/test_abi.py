@@ -202,7 +202,11 @@ def test_plan_held_rows_region():
     assert plan(2, 9 * 256, 8192)["path"] == 3 and plan(2, 9 * 256 + 1, 8192)["path"] == 2
     assert plan(4, 16 * 256, 4096)["path"] == 3 and plan(4, 16 * 256 + 1, 4096)["path"] == 2
     assert plan(5, 2048, 7168) == {"path": 3, "waves": 8, "chunks": 2, "grid": 256}
-    assert plan(16, 4096, 4096)["path"] == 3 and plan(5, 2048, 7168, 2)["path"] != 3
+    assert plan(16, 4096, 4096)["path"] == 3
+    # fp32 partials: 4 wavefronts, beyond 4 shards where shards x chunks <= 48
+    assert plan(5, 2048, 7168, 2) == {"path": 3, "waves": 4, "chunks": 4, "grid": 256}
+    assert plan(12, 2048, 8192, 2)["path"] == 3 and plan(16, 2048, 4096, 2)["path"] == 3
+    assert plan(16, 2048, 7168, 2)["path"] != 3
     assert plan(4, 2048, 4088)["path"] != 3 and plan(4, 2048, 4096)["path"] == 3
     assert plan(4, 2048, 8200)["path"] == 2
     # the thresholds scale with the CU count

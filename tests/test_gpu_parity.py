@@ -942,6 +942,20 @@ def test_held_rows_with_eight_wavefronts_every_row(shape):
     compare(got4, ref, "%s, 4 wavefronts" % (shape,))
 
 
+@pytest.mark.parametrize("shape", [(8, 2048, 7168), (16, 1536, 4096)])
+def test_held_rows_fp32_many_shards_every_row(shape):
+    # fp32 partials beyond 4 shards in the held-row region: the plan takes the 4-wavefront
+    # form without a quantised copy; every row against the oracle
+    n, t, h = shape
+    w = _case(n, t, h, "f32", "bf16", 616, quant=None)
+    plan = arf.arf_get_plan(n, t, h, 2)
+    assert plan["path"] == 3 and plan["waves"] == 4, plan
+    say("held rows, fp32 partials, %s" % (shape,))
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    ref = run_oracle(p, r, g, w.eps, "f32", "bf16")
+    compare(run_gpu(pd_, rd, gd, w.eps, "bf16"), ref, "f32 %s, held rows" % (shape,))
+
+
 # ---- HIP graph capture --------------------------------------------------------------------
 
 @pytest.mark.parametrize("path", [0, 4])
