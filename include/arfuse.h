@@ -222,8 +222,8 @@ arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
  * TEST AND TUNING ONLY; process-wide, not to be changed while other threads call the
  * library. path 0 = automatic (the other two arguments must be 0); 1 = one row per
  * wavefront; 2 = one row per workgroup, rows by workgroup index; 3 = held rows (4 or 8
- * wavefronts, 8 only for 16-bit partials, 1-4 shards and no quantised copy, the automatic
- * choice there; rows of up to 16384 elements; arf_reduce_rows keeps its automatic plan);
+ * wavefronts, 8 only for 16-bit partials without a quantised copy, the automatic choice
+ * there; rows of up to 16384 elements; arf_reduce_rows keeps its automatic plan);
  * 4 = one row per workgroup with EVERY row claimed from the stream's counters (4 of them
  * for rows of less than 96 KiB of traffic, 2 below 256 KiB, else 1; where a call may
  * claim; a grid beyond one dispatch runs path 2). waves_per_block (paths 2 and 4: 4, 8
