@@ -163,7 +163,7 @@ int main() {
                     // limit of one dispatch, or is split by the caller into row ranges
                     if (o[0] != 2 && o[0] != 1) EXPECT((int64_t)(uint32_t)o[3] * lanes <= (int64_t)UINT32_MAX);
                     if (o[0] == 3) {
-                        EXPECT(t >= 6LL * cus && t <= 16LL * cus && h >= 4096 && h <= 8192);
+                        EXPECT(t >= 3LL * cus && t <= 16LL * cus && h >= 4096 && h <= 8192);   // bf16
                         EXPECT(div_up_i64(t, cus) * (2LL * h + 12LL * o[1]) <= 160 * 1024);
                     }
                 }

@@ -162,7 +162,7 @@ def test_plan_for_the_named_workloads():
     assert plan(2, 16, 1024)["path"] == 2
     assert plan(4, 4096, 7168) == {"path": 2, "waves": 4, "chunks": 4, "grid": 4096}
     assert plan(4, 4096, 7168, 2) == {"path": 4, "waves": 4, "chunks": 4, "grid": 4096 + 256}
-    assert plan(2, 1024, 4096) == {"path": 2, "waves": 4, "chunks": 2, "grid": 1024}
+    assert plan(2, 1024, 4096) == {"path": 3, "waves": 8, "chunks": 1, "grid": 256}
     assert plan(8, 8192, 65536) == {"path": 2, "waves": 16, "chunks": 8, "grid": 8192}
 
 
@@ -203,6 +203,9 @@ def test_plan_held_rows_region():
     assert plan(4, 16 * 256, 4096)["path"] == 3 and plan(4, 16 * 256 + 1, 4096)["path"] == 2
     assert plan(5, 2048, 7168) == {"path": 3, "waves": 8, "chunks": 2, "grid": 256}
     assert plan(16, 4096, 4096)["path"] == 3
+    # 16-bit partials (8 wavefronts) from 3 rows per CU, fp32 ones from 6
+    assert plan(8, 767, 4096)["path"] != 3 and plan(8, 768, 4096)["path"] == 3
+    assert plan(4, 1535, 7168, 2)["path"] != 3
     # fp32 partials: 4 wavefronts, beyond 4 shards where shards x chunks <= 48
     assert plan(5, 2048, 7168, 2) == {"path": 3, "waves": 4, "chunks": 4, "grid": 256}
     assert plan(12, 2048, 8192, 2)["path"] == 3 and plan(16, 2048, 4096, 2)["path"] == 3
