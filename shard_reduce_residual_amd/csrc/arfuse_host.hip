@@ -161,10 +161,9 @@ bool held_plan(int64_t rows, int32_t hidden, const DeviceInfo& dev, int waves, i
 //      compute unit;
 //    - rows too wide for 8 chunks per lane use 16 wavefronts.
 //  * held rows (path 3) where that measured faster (sweep of 175 shapes, bit-identical
-//    outputs, and 40 more with 5-16 shards, see held_eight): 4096 <= hidden <= 8192, no
-//    quantised copy, 6 (3 for 16-bit partials) to 16 rows per compute unit, no more than
-//    one batch per workgroup holds; for fp32 partials beyond 4 shards, shards x chunks per
-//    lane <= 48. There HBM sees the whole
+//    outputs, and 116 more, see held_eight and held_wins): 4096 <= hidden <= 8192, no
+//    quantised copy, from 3 rows per compute unit up to what one batch per workgroup
+//    holds; for fp32 partials beyond 4 shards, shards x chunks per lane <= 48. There HBM sees the whole
 //    launch's reads, then its writes: 2-10% faster (3% for 4 fp32 shards of 2048 x 7168). With more shards, other
 //    row sizes, several batches, or the per-token scale's extra pass over the held rows, it
 //    was slower than one row per workgroup.
@@ -202,11 +201,12 @@ bool held_eight(int pdt, int quant, int32_t hidden) {
 bool held_wins(int64_t tokens, int32_t hidden, int n, int quant, int pdt, const DeviceInfo& dev,
                Plan* pl) {
     const bool eight = held_eight(pdt, quant, hidden);
-    // from 3 rows per CU with 8 wavefronts (3-5 rows per CU, 4-16 shards, hidden 4096 and
-    // 8192: 1-12% faster on all 18 shapes), from 6 with 4; hidden 2048 was 23-38% slower
-    if (hidden < 4096 || hidden > 8192 || quant != arf::kQuantNone ||
-        tokens < (eight ? 3LL : 6LL) * dev.cus || tokens > 16LL * dev.cus)
-        return false;
+    // From 3 rows per CU (3-5 rows per CU, 2-16 shards, hidden 4096-8192: 1-12% faster
+    // than rows by index on all 36 shapes, 16-bit and fp32) up to as many as one batch
+    // holds (17-19 rows per CU of hidden 4096: up to 9% faster, level for 2 bf16 shards).
+    // Hidden 2048 was 23-38% slower than one row per wavefront.
+    const bool held_region = hidden >= 4096 && hidden <= 8192 && tokens >= 3LL * dev.cus;
+    if (!held_region || quant != arf::kQuantNone) return false;
     Plan h;
     if (!held_plan(tokens, hidden, dev, eight ? 8 : 4, 0, &h)) return false;
     // fp32 partials beyond 4 shards: the 4-wavefront form without a quantised copy, where

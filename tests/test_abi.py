@@ -148,7 +148,8 @@ def test_plan_covers_the_row_and_follows_the_menu():
                     else:   # held rows: one workgroup per CU, one batch of rows each;
                         # 8 wavefronts for 16-bit partials (these are bf16)
                         assert p["path"] == 3 and p["waves"] == 8
-                        assert p["grid"] == min(t, 256) and 6 * 256 <= t <= 16 * 256
+                        assert p["grid"] == min(t, 256) and t >= 3 * 256
+                        assert -(-t // 256) * (2 * h + 96) <= 160 * 1024
     finally:
         arf.arf_set_path_override(0)
 
@@ -189,7 +190,7 @@ def test_plan_row_per_wave_region():
     assert plan(4, 8191, 2056, 2)["path"] == 2          # 257 chunks
     assert plan(4, 8192, 2056, 2)["path"] == 4          # 257 chunks, claimed from 32 per CU
     for t in (512, 1024, 2048, 4096, 8191):   # never one row per wavefront (held rows at
-        assert plan(8, t, 4096)["path"] != 1      # 6-16 rows per CU)
+        assert plan(8, t, 4096)["path"] != 1      # 3-19 rows per CU)
     # the thresholds scale with the CU count
     assert plan(8, 1023, 2048, 0, 128)["path"] == 2 and plan(8, 1024, 2048, 0, 128)["path"] == 1
 
@@ -197,15 +198,14 @@ def test_plan_row_per_wave_region():
 def test_plan_held_rows_region():
     # held rows only where measured faster: <= 4 shards, 4096 <= hidden <= 8192, 6 to 16
     # rows per CU, one batch per workgroup (LDS holds 11 rows of 7168, 9 of 8192)
-    assert plan(4, 1535, 7168, 2)["path"] == 2 and plan(4, 1536, 7168, 2)["path"] == 3
+    assert plan(4, 767, 7168, 2)["path"] != 3 and plan(4, 768, 7168, 2)["path"] == 3
     assert plan(4, 11 * 256, 7168, 2)["path"] == 3 and plan(4, 11 * 256 + 1, 7168, 2)["path"] == 2
     assert plan(2, 9 * 256, 8192)["path"] == 3 and plan(2, 9 * 256 + 1, 8192)["path"] == 2
-    assert plan(4, 16 * 256, 4096)["path"] == 3 and plan(4, 16 * 256 + 1, 4096)["path"] == 2
+    assert plan(4, 19 * 256, 4096)["path"] == 3 and plan(4, 19 * 256 + 1, 4096)["path"] != 3
     assert plan(5, 2048, 7168) == {"path": 3, "waves": 8, "chunks": 2, "grid": 256}
     assert plan(16, 4096, 4096)["path"] == 3
-    # 16-bit partials (8 wavefronts) from 3 rows per CU, fp32 ones from 6
+    # from 3 rows per CU, 16-bit (8 wavefronts) and fp32 (4) partials alike
     assert plan(8, 767, 4096)["path"] != 3 and plan(8, 768, 4096)["path"] == 3
-    assert plan(4, 1535, 7168, 2)["path"] != 3
     # fp32 partials: 4 wavefronts, beyond 4 shards where shards x chunks <= 48
     assert plan(5, 2048, 7168, 2) == {"path": 3, "waves": 4, "chunks": 4, "grid": 256}
     assert plan(12, 2048, 8192, 2)["path"] == 3 and plan(16, 2048, 4096, 2)["path"] == 3
@@ -213,7 +213,7 @@ def test_plan_held_rows_region():
     assert plan(4, 2048, 4088)["path"] != 3 and plan(4, 2048, 4096)["path"] == 3
     assert plan(4, 2048, 8200)["path"] == 2
     # the thresholds scale with the CU count
-    assert plan(4, 767, 7168, 2, 128)["path"] == 2 and plan(4, 768, 7168, 2, 128)["path"] == 3
+    assert plan(4, 383, 7168, 2, 128)["path"] != 3 and plan(4, 384, 7168, 2, 128)["path"] == 3
 
 
 def test_plan_claim_region():
