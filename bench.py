@@ -142,8 +142,8 @@ def percentiles_us(ms_sorted):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c4", help="c0..c4 (default c4)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target oracle time for the CPU baseline (0: skip it)")
