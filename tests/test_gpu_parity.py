@@ -956,6 +956,29 @@ def test_held_rows_fp32_many_shards_every_row(shape):
     compare(run_gpu(pd_, rd, gd, w.eps, "bf16"), ref, "f32 %s, held rows" % (shape,))
 
 
+
+@pytest.mark.parametrize("pd,quant", [("bf16", None), ("bf16", "per_token"), ("f32", "per_tensor")])
+def test_held_rows_beyond_64_per_batch(pd, quant):
+    # The held-row kernel forms the inverse RMS of its first 64 held rows in parallel, one
+    # per lane, and of any further row in turn. Rows of 64 elements take about 700 to a
+    # batch, so 25677 rows give each of the 256 workgroups one batch of 100 or 101 rows
+    # (4 shards; 8 wavefronts without a copy, 4 with one); every row against the oracle.
+    n, t, h = 4, 25677, 64
+    w = _case(n, t, h, pd, "bf16", 617, quant=quant)
+    say("held rows beyond 64 per batch, %s %s" % (pd, quant))
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    ref = run_oracle(p, r, g, w.eps, pd, "bf16", quant=quant,
+                     scale_in=0.02 if quant == "per_tensor" else None)
+    try:
+        arf.arf_set_path_override(3)
+        plan = arf.arf_get_plan(n, t, h, {"bf16": 0, "f32": 2}[pd])
+        assert plan["path"] == 3 and plan["grid"] == min(t, torch.cuda.get_device_properties(0).multi_processor_count), plan
+        got = run_gpu(pd_, rd, gd, w.eps, "bf16", quant=quant, scale=0.02)
+    finally:
+        arf.arf_set_path_override(0)
+    compare(got, ref, "held rows, %s %s, %d rows of %d" % (pd, quant, t, h))
+
+
 # ---- HIP graph capture --------------------------------------------------------------------
 
 @pytest.mark.parametrize("path", [0, 4])
