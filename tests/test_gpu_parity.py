@@ -48,8 +48,10 @@ class Out:
 
 
 def run_gpu(p, r, g, eps, act, *, res=True, norm=True, quant=None, scale=None,
-            in_place=False):
-    """p, r, g: device tensors. Returns host numpy results (uint16 bits / uint8 / f32)."""
+            in_place=False, stream=None):
+    """p, r, g: device tensors. Returns host numpy results (uint16 bits / uint8 / f32).
+    ``stream``: a stream handle for the call (default: torch's current stream); the call
+    then starts after a device synchronisation."""
     t, h = r.shape
     adt = TORCH[act]
     rin = r.clone() if in_place else r
@@ -63,9 +65,11 @@ def run_gpu(p, r, g, eps, act, *, res=True, norm=True, quant=None, scale=None,
         rout_t = None
     nout = Out((t, h), adt) if norm else None
     out = {}
+    if stream is not None:
+        torch.cuda.synchronize()
     if quant is None:
         arf.arf_reduce_add_rmsnorm(p, rin, g, eps, residual_out=rout_t,
-                                   norm_out=nout.t if nout else None)
+                                   norm_out=nout.t if nout else None, stream=stream)
     else:
         q = Out((t, h), torch.uint8)
         sin = sout = None
@@ -75,10 +79,12 @@ def run_gpu(p, r, g, eps, act, *, res=True, norm=True, quant=None, scale=None,
         else:
             sout = Out((t,), torch.float32)
             mode = arf.ARF_QUANT_PER_TOKEN
+        if stream is not None:
+            torch.cuda.synchronize()
         arf.arf_reduce_add_rmsnorm_quant(p, rin, g, eps, q.t, mode, scale_in=sin,
                                          scale_out=sout.t if sout else None,
                                          residual_out=rout_t,
-                                         norm_out=nout.t if nout else None)
+                                         norm_out=nout.t if nout else None, stream=stream)
         torch.cuda.synchronize()
         assert q.canary_ok()
         out["quant_out"] = q.t.cpu().numpy()
@@ -915,6 +921,25 @@ def test_split_claim_plans_every_row(shape):
     for k in range(2):
         got = run_gpu(pd_, rd, gd, w.eps, "bf16", quant=quant)
         compare(got, ref, "%s, call %d" % (shape, k))
+
+
+HIP_STREAM_PER_THREAD = 2   # the value of hipStreamPerThread in hip_runtime_api.h
+
+
+def test_per_thread_and_legacy_default_streams():
+    # a shape whose plan claims rows, on the per-thread default stream (where the library
+    # takes rows by workgroup index instead: one handle stands for a different stream in
+    # every thread) and on the legacy default stream (handle 0, which claims); every row
+    # against the oracle
+    n, t, h = 8, 8192, 2048
+    w = _case(n, t, h, "bf16", "bf16", 618, quant="per_token")
+    assert arf.arf_get_plan(n, t, h, 0)["path"] == 4
+    say("per-thread and legacy default streams")
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    ref = run_oracle(p, r, g, w.eps, "bf16", "bf16", quant="per_token")
+    for handle in (HIP_STREAM_PER_THREAD, 0):
+        got = run_gpu(pd_, rd, gd, w.eps, "bf16", quant="per_token", stream=handle)
+        compare(got, ref, "stream handle %d" % handle)
 
 
 @pytest.mark.parametrize("shape", [(2, 2048, 7168, "bf16"), (4, 4096, 4096, "f16"),
