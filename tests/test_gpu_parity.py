@@ -663,6 +663,25 @@ def test_reduce_rows_and_twoshot_composition(pd, ad):
     compare(one, run_oracle(p, r, g, w.eps, pd, ad, quant="per_token"), "oneshot")
 
 
+
+def test_reduce_rows_with_claimed_rows():
+    # a reduce-only row range large enough for the plan to claim its rows (2100 rows of
+    # 8 x 16384 bf16), twice on one stream, against the oracle; rows outside keep their poison
+    n, t, h = 8, 4096, 16384
+    beg, cnt = 1000, 2100
+    w = _case(n, t, h, "bf16", "bf16", 701)
+    assert arf.arf_get_plan(n, cnt, h, 0)["path"] == 4
+    say("reduce rows with claimed rows")
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    ref = oracle.reduce_rows(workloads.to_bits(p), partial_dtype="bf16", act_dtype="bf16",
+                             rows=(beg, cnt), out_init=POISON, n_threads=THREADS)
+    for k in range(2):
+        out = Out((t, h), torch.bfloat16)
+        arf.arf_reduce_rows(pd_, out.t, row_begin=beg, row_count=cnt)
+        torch.cuda.synchronize()
+        assert out.canary_ok()
+        assert np.array_equal(workloads.to_bits(out.t), ref), k
+
 # ---- OCP MXFP4 copy ------------------------------------------------------------------------
 
 def _ord4(c):
