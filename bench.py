@@ -131,6 +131,16 @@ class Runner:
         return sorted(e0.elapsed_time(e1) for e0, e1 in ev)
 
 
+def plan_of(w):
+    """The launch plan of the workload's call (its quantised copy included)."""
+    import shard_reduce_residual_amd as arf
+
+    quant = {None: arf.ARF_QUANT_NONE, "per_tensor": arf.ARF_QUANT_PER_TENSOR,
+             "per_token": arf.ARF_QUANT_PER_TOKEN}[w.quant]
+    return arf.arf_get_plan_quant(w.n_shards, w.tokens, w.hidden,
+                                  {"bf16": 0, "f16": 1, "f32": 2}[w.partial_dtype], quant)
+
+
 def percentiles_us(ms_sorted):
     """median, p10 and p90 (µs) of sorted per-launch durations in ms."""
     def at(q):
@@ -195,7 +205,7 @@ def survey(args, dev, stream):
                                 partial_dtype=pdt, quant=quant)
         B = w.algorithmic_bytes()
         run = Runner(w, dev, stream, sets=max(1, min(6, -(-1_500_000_000 // B))))
-        plan = arf.arf_get_plan(n, t, h, arf.ARF_F32 if pdt == "f32" else arf.ARF_BF16)
+        plan = plan_of(w)
         _, kms = run.measure(args.steps, args.warmup)
         d = direction_probes(w, [s[0] for s in run.sets], stream, reps=8)
         gbs = B / (kms * 1e-3) / 1e9
@@ -335,8 +345,7 @@ def main():
                      "achieved": round(B2 / (kms2 * 1e-3) / 1e9, 2), "unit": "GB/s",
                      "frac": round(B2 / (kms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "tokens_per_s": round(w2.tokens / (kms2 * 1e-3), 1),
-                     "plan": arf.arf_get_plan(w2.n_shards, w2.tokens, w2.hidden,
-                                              {"bf16": 0, "f16": 1, "f32": 2}[w2.partial_dtype]),
+                     "plan": plan_of(w2),
                      "traffic": read_traffic(w2.name),
                      "row_mix_GBs": mix2,
                      "frac_of_row_mix_probe": None if mix2 is None else
@@ -365,7 +374,7 @@ def main():
     if not args.no_copy_probe:
         probes = hbm_probes(w, p, stream)
 
-    plan = arf.arf_get_plan(w.n_shards, t, h, {"bf16": 0, "f16": 1, "f32": 2}[w.partial_dtype])
+    plan = plan_of(w)
     line = {
         "metric": METRIC,
         "value": round(value, 2),

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define ARF_VERSION 300 /* 0.3.0 */
+#define ARF_VERSION 400 /* 0.4.0 */
 
 /* Element types (arguments typed int32_t take these values). */
 #define ARF_BF16 0
@@ -67,7 +67,8 @@ extern "C" {
 #define ARF_ACC_F32 0
 #define ARF_ACC_PARTIAL 1
 
-/* Quantised-copy modes. */
+/* Quantised-copy modes (ARF_QUANT_NONE: no copy, for arf_get_plan_quant only). */
+#define ARF_QUANT_NONE (-1)
 #define ARF_QUANT_PER_TENSOR 0 /* fp8-e4m3, y ~ code * scale_in[0], scale given by the caller */
 #define ARF_QUANT_PER_TOKEN 1  /* fp8-e4m3, scale_out[t] = max_i |y[t][i]| / 448, written    */
 #define ARF_QUANT_MXFP4 2      /* OCP MXFP4 (arf_fused_epilogue only): blocks of 32 E2M1
@@ -217,6 +218,17 @@ int32_t arf_version(void);
  */
 arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
                         int32_t partial_dtype, int32_t num_cus, int32_t* out);
+
+/*
+ * The same for a call with the quantised copy `quant_mode` (ARF_QUANT_NONE, which gives
+ * arf_get_plan's answer, ARF_QUANT_PER_TENSOR, ARF_QUANT_PER_TOKEN or ARF_QUANT_MXFP4; any
+ * other value: ARF_ERR_VALUE; MXFP4 with hidden % 32 != 0: ARF_ERR_SHAPE). The plan depends on
+ * the copy where the held rows (path 3) are concerned: they take no per-token or MXFP4 copy,
+ * and a per-tensor one only in part of their range.
+ */
+arf_status arf_get_plan_quant(int32_t n_shards, int64_t tokens, int32_t hidden,
+                              int32_t partial_dtype, int32_t quant_mode, int32_t num_cus,
+                              int32_t* out);
 
 /*
  * TEST AND TUNING ONLY; process-wide, not to be changed while other threads call the

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libarfuse.so")
 
 ARF_BF16, ARF_F16, ARF_F32 = 0, 1, 2
-ARF_QUANT_PER_TENSOR, ARF_QUANT_PER_TOKEN, ARF_QUANT_MXFP4 = 0, 1, 2
+ARF_QUANT_NONE, ARF_QUANT_PER_TENSOR, ARF_QUANT_PER_TOKEN, ARF_QUANT_MXFP4 = -1, 0, 1, 2
 ARF_ACC_F32, ARF_ACC_PARTIAL = 0, 1
 ARF_MAX_SHARDS, ARF_MAX_HIDDEN = 16, 65536
 STATUS = ["ARF_OK", "ARF_ERR_NULL", "ARF_ERR_SHAPE", "ARF_ERR_DTYPE", "ARF_ERR_ALIGN",
@@ -47,6 +47,7 @@ SIGNATURES = {
     "arf_status_string": (ctypes.c_char_p, [_i32]),
     "arf_version": (_i32, []),
     "arf_get_plan": (_i32, [_i32, _i64, _i32, _i32, _i32, ctypes.POINTER(_i32)]),
+    "arf_get_plan_quant": (_i32, [_i32, _i64, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32)]),
     "arf_set_path_override": (_i32, [_i32, _i32, _i32]),
     "arf_e4m3_encode": (_i32, [_vp, _vp, _i64, _vp]),
     "arf_stream_copy": (_i32, [_vp, _vp, _i64, _vp]),
@@ -245,6 +246,14 @@ def arf_get_plan(n_shards: int, tokens: int, hidden: int, partial_dtype: int,
     out = (_i32 * 4)()
     _check(lib().arf_get_plan(n_shards, tokens, hidden, partial_dtype, num_cus, out),
            "arf_get_plan")
+    return {"path": out[0], "waves": out[1], "chunks": out[2], "grid": out[3]}
+
+
+def arf_get_plan_quant(n_shards: int, tokens: int, hidden: int, partial_dtype: int,
+                       quant_mode: int, num_cus: int = 0) -> dict:
+    out = (_i32 * 4)()
+    _check(lib().arf_get_plan_quant(n_shards, tokens, hidden, partial_dtype, quant_mode,
+                                    num_cus, out), "arf_get_plan_quant")
     return {"path": out[0], "waves": out[1], "chunks": out[2], "grid": out[3]}
 
 

@@ -161,12 +161,13 @@ bool held_plan(int64_t rows, int32_t hidden, const DeviceInfo& dev, int waves, i
 //      compute unit;
 //    - rows too wide for 8 chunks per lane use 16 wavefronts.
 //  * held rows (path 3) where that measured faster (sweep of 175 shapes, bit-identical
-//    outputs, and 116 more, see held_eight and held_wins): 4096 <= hidden <= 8192, no
+//    outputs, and 150 more, see held_eight and held_wins): 4096 <= hidden <= 8192, no
 //    quantised copy, from 3 rows per compute unit up to what one batch per workgroup
-//    holds; for fp32 partials beyond 4 shards, shards x chunks per lane <= 48. There HBM sees the whole
-//    launch's reads, then its writes: 2-10% faster (3% for 4 fp32 shards of 2048 x 7168). With more shards, other
-//    row sizes, several batches, or the per-token scale's extra pass over the held rows, it
-//    was slower than one row per workgroup.
+//    holds; for fp32 partials beyond 4 shards, shards x chunks per lane <= 48; with a
+//    per-tensor fp8 copy, part of that range. There HBM sees the whole launch's reads,
+//    then its writes: 2-10% faster (3% for 4 fp32 shards of 2048 x 7168). With more
+//    shards, other row sizes, several batches, or the per-token scale's extra pass over the
+//    held rows, it was slower than one row per workgroup.
 //  * rows claimed in start order (path 4, the same kernel as path 2) where a sweep of 32
 //    shapes (1-16 shards, hidden 4096-16384, 1024-16384 tokens, bf16 and fp32 partials)
 //    measured it faster: 4 wavefronts per row, and either at least 16 rows per compute unit
@@ -206,13 +207,24 @@ bool held_wins(int64_t tokens, int32_t hidden, int n, int quant, int pdt, const 
     // holds (17-19 rows per CU of hidden 4096: up to 9% faster, level for 2 bf16 shards).
     // Hidden 2048 was 23-38% slower than one row per wavefront.
     const bool held_region = hidden >= 4096 && hidden <= 8192 && tokens >= 3LL * dev.cus;
-    if (!held_region || quant != arf::kQuantNone) return false;
+    if (!held_region) return false;
+    if (quant == arf::kQuantTensor) {
+        // A per-tensor fp8 copy (the general 4-wavefront form): from 4 rows per CU with
+        // hidden 6144-8192, 2-4 16-bit shards or 2-8 fp32 shards, 0.6-9% faster than rows
+        // by index on all 16 shapes measured (4 x 2048 x 7168: 39.9 -> 36.5 us). With more
+        // 16-bit shards (-1.2% to +12%), one shard, hidden 4096-5120 (-4% to +14%) or 3 rows
+        // per CU (-1.7% to +3.2%) it was not faster throughout.
+        const int max_n = pdt == ARF_F32 ? 8 : 4;
+        if (hidden < 6144 || n < 2 || n > max_n || tokens < 4LL * dev.cus) return false;
+    } else if (quant != arf::kQuantNone) {
+        return false;
+    }
     Plan h;
     if (!held_plan(tokens, hidden, dev, eight ? 8 : 4, 0, &h)) return false;
-    // fp32 partials beyond 4 shards: the 4-wavefront form without a quantised copy, where
-    // shards x chunks per lane <= 48 (5-16 shards, 6-16 rows per CU: 0.5-10% faster than
-    // rows by index or claims on 34 of 40 shapes; 16 shards x 4 chunks ran out of
-    // registers, 16-23% slower)
+    // fp32 partials beyond 4 shards: the 4-wavefront form, where shards x chunks per lane
+    // <= 48 (without a copy, 5-16 shards, 6-16 rows per CU: 0.5-10% faster than rows by
+    // index or claims on 34 of 40 shapes; 16 shards x 4 chunks ran out of registers, 16-23%
+    // slower)
     if (!eight && n > 4 && (h.chunks > 4 || n * h.chunks > 48)) return false;
     if ((int64_t)h.grid * h.held < tokens) return false;   // more than one batch
     *pl = h;
@@ -730,30 +742,47 @@ const char* arf_status_string(int32_t s) {
 
 int32_t arf_version(void) { return ARF_VERSION; }
 
-arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
-                        int32_t partial_dtype, int32_t num_cus, int32_t* out) {
+arf_status arf_get_plan_quant(int32_t n_shards, int64_t tokens, int32_t hidden,
+                              int32_t partial_dtype, int32_t quant_mode, int32_t num_cus,
+                              int32_t* out) {
     if (!out) return ARF_ERR_NULL;
     if (n_shards < 1 || n_shards > ARF_MAX_SHARDS || tokens < 0 || tokens > INT32_MAX ||
         hidden <= 0 || hidden % 8 != 0 || hidden > ARF_MAX_HIDDEN)
         return ARF_ERR_SHAPE;
     if (partial_dtype != ARF_BF16 && partial_dtype != ARF_F16 && partial_dtype != ARF_F32)
         return ARF_ERR_DTYPE;
+    int32_t q;
+    if (quant_mode == ARF_QUANT_NONE) q = arf::kQuantNone;
+    else if (quant_mode == ARF_QUANT_PER_TENSOR) q = arf::kQuantTensor;
+    else if (quant_mode == ARF_QUANT_PER_TOKEN) q = arf::kQuantToken;
+    else if (quant_mode == ARF_QUANT_MXFP4) q = arf::kQuantMx;
+    else return ARF_ERR_VALUE;
+    if (q == arf::kQuantMx && hidden % 32 != 0) return ARF_ERR_SHAPE;
     DeviceInfo dev{num_cus, kPlanLdsBytes, -1};
     if (num_cus <= 0) {
         arf_status st = device_info(&dev);
         if (st != ARF_OK) return st;
     }
+    const int64_t qbytes = q == arf::kQuantMx     ? hidden / 2 + hidden / 32
+                           : q != arf::kQuantNone ? hidden
+                                                  : 0;
     const int64_t row_bytes = (int64_t)n_shards * hidden * (partial_dtype == ARF_F32 ? 4 : 2) +
-                              2LL * hidden * 3;
+                              2LL * hidden * 3 + qbytes;
     Plan pl;
-    arf_status st = make_plan(tokens, hidden, n_shards, partial_dtype, arf::kQuantNone, row_bytes,
-                              dev, false, &pl);
+    arf_status st = make_plan(tokens, hidden, n_shards, partial_dtype, q, row_bytes, dev, false,
+                              &pl);
     if (st != ARF_OK) return st;
     out[0] = pl.path;
     out[1] = pl.waves;
     out[2] = pl.chunks;
     out[3] = (int32_t)pl.grid;
     return ARF_OK;
+}
+
+arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
+                        int32_t partial_dtype, int32_t num_cus, int32_t* out) {
+    return arf_get_plan_quant(n_shards, tokens, hidden, partial_dtype, ARF_QUANT_NONE, num_cus,
+                              out);
 }
 
 arf_status arf_set_path_override(int32_t path, int32_t waves_per_block,

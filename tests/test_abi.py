@@ -27,7 +27,7 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     L = arf.lib()
     names = declared_symbols()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(arf.SIGNATURES)
@@ -47,7 +47,7 @@ def test_library_exports_nothing_else():
 
 
 def test_version_and_status_strings():
-    assert arf.arf_version() == 300
+    assert arf.arf_version() == 400
     for code, name in enumerate(arf.STATUS):
         assert arf.arf_status_string(code).startswith(name)
     assert "unknown" in arf.arf_status_string(99)
@@ -215,6 +215,37 @@ def test_plan_held_rows_region():
     # the thresholds scale with the CU count
     assert plan(4, 383, 7168, 2, 128)["path"] != 3 and plan(4, 384, 7168, 2, 128)["path"] == 3
 
+
+
+def qplan(n, t, h, quant, pd=0, cus=256):
+    return arf.arf_get_plan_quant(n, t, h, pd, quant, cus)
+
+
+def test_plan_with_a_quantised_copy():
+    # the plan of a call with a copy: ARF_QUANT_NONE is arf_get_plan's answer
+    for args in [(4, 2048, 7168, 2), (8, 8192, 16384, 0), (2, 16, 1024, 0), (8, 64, 8192, 0)]:
+        assert qplan(*args[:3], arf.ARF_QUANT_NONE, args[3]) == plan(*args)
+    # held rows take no per-token or MXFP4 copy
+    for q in (arf.ARF_QUANT_PER_TOKEN, arf.ARF_QUANT_MXFP4):
+        assert qplan(4, 2048, 7168, q, 2)["path"] == 2
+        assert qplan(2, 2048, 8192, q)["path"] != 3
+    # a per-tensor copy: from 4 rows per CU, hidden 6144-8192, 2-4 16-bit or 2-8 fp32 shards
+    t = arf.ARF_QUANT_PER_TENSOR
+    assert qplan(4, 2048, 7168, t, 2) == {"path": 3, "waves": 4, "chunks": 4, "grid": 256}
+    assert qplan(2, 2048, 8192, t) == {"path": 3, "waves": 4, "chunks": 4, "grid": 256}
+    assert qplan(4, 1023, 8192, t)["path"] != 3 and qplan(4, 1024, 8192, t)["path"] == 3
+    assert qplan(4, 2048, 6144, t)["path"] == 3 and qplan(4, 2048, 6136, t)["path"] != 3
+    assert qplan(1, 2048, 8192, t, 1)["path"] != 3 and qplan(2, 2048, 8192, t, 1)["path"] == 3
+    assert qplan(5, 2048, 7168, t)["path"] != 3 and qplan(8, 1536, 7168, t, 2)["path"] == 3
+    assert qplan(9, 1536, 7168, t, 2)["path"] != 3
+    assert qplan(4, 2048, 4096, t)["path"] != 3 and plan(4, 2048, 4096)["path"] == 3
+    # one batch per workgroup, as without a copy
+    assert qplan(2, 9 * 256, 8192, t)["path"] == 3 and qplan(2, 9 * 256 + 1, 8192, t)["path"] != 3
+    # argument checks
+    with pytest.raises(arf.ArfError):
+        qplan(4, 2048, 7168, 3)
+    with pytest.raises(arf.ArfError):
+        qplan(4, 2048, 7176, arf.ARF_QUANT_MXFP4)
 
 def test_plan_claim_region():
     # rows claimed in start order: 4 wavefronts per row, and >= 16 rows per CU with >= 128

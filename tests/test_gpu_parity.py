@@ -1023,6 +1023,24 @@ def test_held_rows_beyond_64_per_batch(pd, quant):
     compare(got, ref, "held rows, %s %s, %d rows of %d" % (pd, quant, t, h))
 
 
+
+@pytest.mark.parametrize("shape", [(4, 2048, 7168, "bf16"), (2, 1024, 8192, "f16"),
+                                   (8, 1536, 7168, "f32"), (3, 1024, 6144, "bf16")])
+def test_held_rows_with_a_per_tensor_copy_every_row(shape):
+    # shapes where the plan takes held rows for a call with a per-tensor fp8 copy (the
+    # general 4-wavefront form); every row against the oracle
+    n, t, h, pd = shape
+    ad = "f16" if pd == "f16" else "bf16"
+    w = _case(n, t, h, pd, ad, 619, quant="per_tensor")
+    plan = arf.arf_get_plan_quant(n, t, h, {"bf16": 0, "f16": 1, "f32": 2}[pd],
+                                  arf.ARF_QUANT_PER_TENSOR)
+    assert plan["path"] == 3 and plan["waves"] == 4, plan
+    say("held rows, per-tensor copy, %s" % (shape,))
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    ref = run_oracle(p, r, g, w.eps, pd, ad, quant="per_tensor", scale_in=0.03)
+    compare(run_gpu(pd_, rd, gd, w.eps, ad, quant="per_tensor", scale=0.03), ref,
+            "per-tensor %s, held rows" % (shape,))
+
 # ---- HIP graph capture --------------------------------------------------------------------
 
 @pytest.mark.parametrize("path", [0, 4])
