@@ -93,18 +93,18 @@ def report(cus: int = 256) -> str:
     for key in ("c0", "c1", "c2", "c3", "c4"):
         w = workloads.WORKLOADS[key]
         pd = {"bf16": 0, "f16": 1, "f32": 2}[w.partial_dtype]
-        # arf_get_plan plans a call without a quantised copy; with one the plan differs only
-        # where it would pick held rows, which none of the quantised workloads reaches
-        plan = arf.arf_get_plan(w.n_shards, w.tokens, w.hidden, pd, cus)
-        assert not (w.quant and plan["path"] == 3)
+        quant = {None: arf.ARF_QUANT_NONE, "per_tensor": arf.ARF_QUANT_PER_TENSOR,
+                 "per_token": arf.ARF_QUANT_PER_TOKEN}[w.quant]
+        plan = arf.arf_get_plan_quant(w.n_shards, w.tokens, w.hidden, pd, quant, cus)
         tu = _tu(w.partial_dtype, w.act_dtype, w.n_shards)
         if tu not in cache:
             cache[tu] = _metadata(tu)
         pt, at = "arf::" + TAG[w.partial_dtype], "arf::" + TAG[w.act_dtype]
         if plan["path"] == 3:
-            # the plan's held calls have no quantised copy: the QUANT = false form
-            name = "void arf::fused_held_rows<%s, %s, %d, %d, %d, false>(arf::Params)" % (
-                pt, at, w.n_shards, plan["chunks"], plan["waves"])
+            # held calls without a quantised copy take the QUANT = false form
+            name = "void arf::fused_held_rows<%s, %s, %d, %d, %d, %s>(arf::Params)" % (
+                pt, at, w.n_shards, plan["chunks"], plan["waves"],
+                "true" if w.quant else "false")
             rows = -(-w.tokens // plan["grid"])
             dyn = rows * (2 * w.hidden + 12 * plan["waves"])
         else:
