@@ -224,7 +224,7 @@ arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
  * arf_get_plan's answer, ARF_QUANT_PER_TENSOR, ARF_QUANT_PER_TOKEN or ARF_QUANT_MXFP4; any
  * other value: ARF_ERR_VALUE; MXFP4 with hidden % 32 != 0: ARF_ERR_SHAPE). The plan depends on
  * the copy where the held rows (path 3) are concerned: they take no per-token or MXFP4 copy,
- * and a per-tensor one only in part of their range.
+ * and a per-tensor one in most of their range, with 4 or 8 wavefronts by shard count.
  */
 arf_status arf_get_plan_quant(int32_t n_shards, int64_t tokens, int32_t hidden,
                               int32_t partial_dtype, int32_t quant_mode, int32_t num_cus,
@@ -233,9 +233,9 @@ arf_status arf_get_plan_quant(int32_t n_shards, int64_t tokens, int32_t hidden,
 /*
  * TEST AND TUNING ONLY; process-wide, not to be changed while other threads call the
  * library. path 0 = automatic (the other two arguments must be 0); 1 = one row per
- * wavefront; 2 = one row per workgroup, rows by workgroup index; 3 = held rows (4 or 8
- * wavefronts, 8 only for 16-bit partials without a quantised copy, the automatic choice
- * there; rows of up to 16384 elements; arf_reduce_rows keeps its automatic plan);
+ * wavefront; 2 = one row per workgroup, rows by workgroup index; 3 = held rows (rows of up
+ * to 16384 elements; 4 or 8 wavefronts, 8 only for 16-bit partials, the automatic choice
+ * there; arf_reduce_rows keeps its automatic plan);
  * 4 = one row per workgroup with EVERY row claimed from the stream's counters (4 of them
  * for rows of less than 96 KiB of traffic, 2 below 256 KiB, else 1; where a call may
  * claim; a grid beyond one dispatch runs path 2). waves_per_block (paths 2 and 4: 4, 8

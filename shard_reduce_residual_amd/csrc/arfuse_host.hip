@@ -164,7 +164,7 @@ bool held_plan(int64_t rows, int32_t hidden, const DeviceInfo& dev, int waves, i
 //    outputs, and 150 more, see held_eight and held_wins): 4096 <= hidden <= 8192, no
 //    quantised copy, from 3 rows per compute unit up to what one batch per workgroup
 //    holds; for fp32 partials beyond 4 shards, shards x chunks per lane <= 48; with a
-//    per-tensor fp8 copy, part of that range. There HBM sees the whole launch's reads,
+//    per-tensor fp8 copy, most of that range (see held_wins). There HBM sees the whole launch's reads,
 //    then its writes: 2-10% faster (3% for 4 fp32 shards of 2048 x 7168). With more
 //    shards, other row sizes, several batches, or the per-token scale's extra pass over the
 //    held rows, it was slower than one row per workgroup.
@@ -188,20 +188,21 @@ bool held_plan(int64_t rows, int32_t hidden, const DeviceInfo& dev, int waves, i
 //    x 4096: -6%; 16 x 16384 x 2048: -9% against one row per wavefront). Rows of 28 KiB
 //    and launches of 16 rows per compute unit gained nothing and keep their plans.
 // The held-row kernel with 8 wavefronts (half the chunks per lane, 2 wavefronts per SIMD)
-// exists for 16-bit partials without a quantised copy, for every shard count. With 1-4
-// shards it measured -7% to +1.6% against 4 wavefronts over the held region (better on
-// balance), and 1% slower for fp32 partials. With 5-16 shards it opens the held region to
-// them: against the plan's rows by index or claims it was 2-12% faster on 38 of 40 shapes
-// (5, 6, 8, 12, 16 shards, hidden 4096-8192, 6-16 rows per CU; 16 x 3072 x 4096: 83.9 ->
-// 73.6 us), level on 8 x 1536 x 4096 and 3% slower on 16 x 2048 x 8192.
-bool held_eight(int pdt, int quant, int32_t hidden) {
-    return pdt != ARF_F32 && quant == arf::kQuantNone &&
-           pow2_at_least(div_up(hidden / 8, 8 * 64)) <= 4;
+// exists for 16-bit partials, for every shard count, without a quantised copy and in the
+// general form. Without a copy, with 1-4 shards it measured -7% to +1.6% against 4
+// wavefronts over the held region (better on balance), and 1% slower for fp32 partials.
+// With 5-16 shards it opens the held region to them: against the plan's rows by index or
+// claims it was 2-12% faster on 38 of 40 shapes (5, 6, 8, 12, 16 shards, hidden 4096-8192,
+// 6-16 rows per CU; 16 x 3072 x 4096: 83.9 -> 73.6 us), level on 8 x 1536 x 4096 and 3%
+// slower on 16 x 2048 x 8192. With a per-tensor copy see held_wins; with a per-token copy
+// (forced held rows only) it was faster than 4 wavefronts on 19 of 24 shapes.
+bool held_eight(int pdt, int32_t hidden) {
+    return pdt != ARF_F32 && pow2_at_least(div_up(hidden / 8, 8 * 64)) <= 4;
 }
 
 bool held_wins(int64_t tokens, int32_t hidden, int n, int quant, int pdt, const DeviceInfo& dev,
                Plan* pl) {
-    const bool eight = held_eight(pdt, quant, hidden);
+    bool eight = held_eight(pdt, hidden);
     // From 3 rows per CU (3-5 rows per CU, 2-16 shards, hidden 4096-8192: 1-12% faster
     // than rows by index on all 36 shapes, 16-bit and fp32) up to as many as one batch
     // holds (17-19 rows per CU of hidden 4096: up to 9% faster, level for 2 bf16 shards).
@@ -209,13 +210,20 @@ bool held_wins(int64_t tokens, int32_t hidden, int n, int quant, int pdt, const 
     const bool held_region = hidden >= 4096 && hidden <= 8192 && tokens >= 3LL * dev.cus;
     if (!held_region) return false;
     if (quant == arf::kQuantTensor) {
-        // A per-tensor fp8 copy (the general 4-wavefront form): from 4 rows per CU with
-        // hidden 6144-8192, 2-4 16-bit shards or 2-8 fp32 shards, 0.6-9% faster than rows
-        // by index on all 16 shapes measured (4 x 2048 x 7168: 39.9 -> 36.5 us). With more
-        // 16-bit shards (-1.2% to +12%), one shard, hidden 4096-5120 (-4% to +14%) or 3 rows
-        // per CU (-1.7% to +3.2%) it was not faster throughout.
-        const int max_n = pdt == ARF_F32 ? 8 : 4;
-        if (hidden < 6144 || n < 2 || n > max_n || tokens < 4LL * dev.cus) return false;
+        // A per-tensor fp8 copy takes the general form, where it measured faster than rows
+        // by index (7 interleaved repetitions each; one shard was not faster throughout):
+        //  - fp32 partials, 4 wavefronts: 2-8 shards, hidden 6144-8192, from 4 rows per CU
+        //    (6 of 6 shapes 0.6-3.2% faster; hidden 4096-5120 and 3 rows per CU mixed);
+        //  - 16-bit partials, 2-4 shards, hidden 6144-8192, from 4 rows per CU: 4 wavefronts
+        //    (10 of 10 shapes 2.8-9.1% faster; 4 x 2048 x 7168: 39.9 -> 36.5 us);
+        //  - 16-bit partials otherwise 8 wavefronts: 2-4 shards below hidden 6144 (9 of 9,
+        //    2.3-6.8%), 5-8 shards (18 of 18, 0.4-7.9%) and 9-16 shards from 8 rows per CU
+        //    (9 of 10, 2.3-9.2%; one +0.6%); 9-16 shards at 3-4 rows per CU were mixed
+        //    (-3.7% to +5.2%).
+        if (n < 2 || tokens < (pdt != ARF_F32 && n > 8 ? 8LL : 3LL) * dev.cus) return false;
+        const bool four = pdt == ARF_F32 || (n <= 4 && hidden >= 6144);
+        if (four && (hidden < 6144 || n > 8 || tokens < 4LL * dev.cus)) return false;
+        eight = eight && !four;
     } else if (quant != arf::kQuantNone) {
         return false;
     }
@@ -275,7 +283,7 @@ arf_status make_plan(int64_t tokens, int32_t hidden, int n, int pdt, int quant,
         // the held-row kernel has no reduce-only form: such calls take the default plan.
         // Without a forced wave count, the plan's: 8 where that form exists and fits.
         if (!reduce_only) {
-            const bool eight = held_eight(pdt, quant, hidden);
+            const bool eight = held_eight(pdt, hidden);
             if (waves == 0 && eight && held_plan(tokens, hidden, dev, 8, chunks, pl)) return ARF_OK;
             if (waves == 8 && !eight) return ARF_ERR_VALUE;
             return held_plan(tokens, hidden, dev, waves ? waves : 4, chunks, pl) ? ARF_OK

@@ -71,10 +71,8 @@ launch_fn pick_shards(int n, bool row_per_wave, int waves, int c) {
 
 // Held-row kernels: 4 wavefronts with C in {1, 2, 4, 8}, in the general form (any quantised
 // copy) for all shard counts and in the form without a quantised copy for 1..4 shards
-// (and for fp32 partials with C in {1, 2, 4}, all shard counts); and 8 wavefronts with C in
-// {1, 2, 4} for 16-bit partials without a quantised copy (all shard counts). The plan
-// takes the forms without a quantised copy: 8 wavefronts (2 per SIMD) for 16-bit partials,
-// 4 for fp32 ones.
+// (and for fp32 partials with C in {1, 2, 4}, all shard counts); and, for 16-bit partials,
+// 8 wavefronts (2 per SIMD) with C in {1, 2, 4} in both forms (all shard counts).
 template <class PT, class AT, int N, int W, bool QUANT, int CMAX>
 held_launch_fn pick_held_c(int c) {
     switch (c) {
@@ -95,7 +93,10 @@ held_launch_fn pick_held(int c, bool quant, int waves) {
         if (!quant && waves == 4 && c <= 4) return pick_held_c<PT, AT, N, 4, false, 4>(c);
     }
     if constexpr (PartTraits<PT>::kPieces == 1) {
-        if (!quant && waves == 8) return pick_held_c<PT, AT, N, 8, false, 4>(c);
+        if (waves == 8) {
+            if (quant) return pick_held_c<PT, AT, N, 8, true, 4>(c);
+            return pick_held_c<PT, AT, N, 8, false, 4>(c);
+        }
     }
     return waves == 4 ? pick_held_c<PT, AT, N, 4, true, 8>(c) : nullptr;
 }

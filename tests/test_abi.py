@@ -229,16 +229,25 @@ def test_plan_with_a_quantised_copy():
     for q in (arf.ARF_QUANT_PER_TOKEN, arf.ARF_QUANT_MXFP4):
         assert qplan(4, 2048, 7168, q, 2)["path"] == 2
         assert qplan(2, 2048, 8192, q)["path"] != 3
-    # a per-tensor copy: from 4 rows per CU, hidden 6144-8192, 2-4 16-bit or 2-8 fp32 shards
+    # a per-tensor copy. fp32 partials: 2-8 shards, hidden 6144-8192, from 4 rows per CU,
+    # 4 wavefronts
     t = arf.ARF_QUANT_PER_TENSOR
     assert qplan(4, 2048, 7168, t, 2) == {"path": 3, "waves": 4, "chunks": 4, "grid": 256}
+    assert qplan(8, 1536, 7168, t, 2)["path"] == 3 and qplan(9, 1536, 7168, t, 2)["path"] != 3
+    assert qplan(4, 2048, 4096, t, 2)["path"] != 3 and qplan(4, 1023, 8192, t, 2)["path"] != 3
+    assert qplan(1, 2048, 8192, t, 2)["path"] != 3
+    # 16-bit partials, 2-4 shards: hidden 6144-8192 from 4 rows per CU with 4 wavefronts,
+    # below 6144 from 3 rows per CU with 8
     assert qplan(2, 2048, 8192, t) == {"path": 3, "waves": 4, "chunks": 4, "grid": 256}
     assert qplan(4, 1023, 8192, t)["path"] != 3 and qplan(4, 1024, 8192, t)["path"] == 3
-    assert qplan(4, 2048, 6144, t)["path"] == 3 and qplan(4, 2048, 6136, t)["path"] != 3
+    assert qplan(4, 2048, 6144, t)["waves"] == 4 and qplan(4, 2048, 6136, t)["waves"] == 8
+    assert qplan(4, 2048, 4096, t) == {"path": 3, "waves": 8, "chunks": 1, "grid": 256}
+    assert qplan(3, 767, 4096, t)["path"] != 3 and qplan(3, 768, 4096, t)["path"] == 3
     assert qplan(1, 2048, 8192, t, 1)["path"] != 3 and qplan(2, 2048, 8192, t, 1)["path"] == 3
-    assert qplan(5, 2048, 7168, t)["path"] != 3 and qplan(8, 1536, 7168, t, 2)["path"] == 3
-    assert qplan(9, 1536, 7168, t, 2)["path"] != 3
-    assert qplan(4, 2048, 4096, t)["path"] != 3 and plan(4, 2048, 4096)["path"] == 3
+    # 5-8 shards from 3 rows per CU, 9-16 from 8, with 8 wavefronts
+    assert qplan(5, 2048, 7168, t) == {"path": 3, "waves": 8, "chunks": 2, "grid": 256}
+    assert qplan(8, 768, 8192, t)["path"] == 3 and qplan(8, 767, 8192, t)["path"] != 3
+    assert qplan(12, 2047, 4096, t)["path"] != 3 and qplan(12, 2048, 4096, t)["waves"] == 8
     # one batch per workgroup, as without a copy
     assert qplan(2, 9 * 256, 8192, t)["path"] == 3 and qplan(2, 9 * 256 + 1, 8192, t)["path"] != 3
     # argument checks

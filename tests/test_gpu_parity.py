@@ -294,7 +294,7 @@ def test_cross_product_sweep_both_paths(pd, ad):
                     compare(got, ref, "n=%d t=%d h=%d path=%s" % (n, t, h, forced or "auto"),
                             min_exact=0.99)
 
-def _geometries(h):
+def _geometries(h, pd="bf16"):
     hc = h // 8
     out = []
     for c in (1, 2, 4, 8):
@@ -305,6 +305,8 @@ def _geometries(h):
                 out.append((2, wv, c))
         if 256 * c >= hc:
             out.append((3, 4, c))   # held rows: 4 wavefronts
+        if pd != "f32" and c <= 4 and 512 * c >= hc:
+            out.append((3, 8, c))   # held rows: 8 wavefronts (16-bit partials)
         for wv in (4, 8, 16):
             if wv * 64 * c >= hc:
                 out.append((4, wv, c))   # one row per workgroup, every row claimed
@@ -731,7 +733,7 @@ def test_mxfp4_every_geometry(pd):
     (p, r, g), (pd_, rd, gd) = upload(w)
     ref = run_oracle(p, r, g, w.eps, pd, "bf16", quant="mxfp4")
     try:
-        for path, wv, c in _geometries(h):
+        for path, wv, c in _geometries(h, pd):
             say("mxfp4 geometry %s path=%d waves=%d chunks=%d" % (pd, path, wv, c))
             arf.arf_set_path_override(path, wv if path != 1 else 0, c)
             compare_mx(run_gpu_mx(pd_, rd, gd, w.eps, "bf16"), ref, "geometry %s" % ((path, wv, c),))
@@ -1024,17 +1026,19 @@ def test_held_rows_beyond_64_per_batch(pd, quant):
 
 
 
-@pytest.mark.parametrize("shape", [(4, 2048, 7168, "bf16"), (2, 1024, 8192, "f16"),
-                                   (8, 1536, 7168, "f32"), (3, 1024, 6144, "bf16")])
+@pytest.mark.parametrize("shape", [(4, 2048, 7168, "bf16", 4), (2, 1024, 8192, "f16", 4),
+                                   (8, 1536, 7168, "f32", 4), (3, 1024, 6144, "bf16", 4),
+                                   (8, 2048, 7168, "bf16", 8), (3, 768, 4096, "f16", 8),
+                                   (12, 2048, 4096, "bf16", 8)])
 def test_held_rows_with_a_per_tensor_copy_every_row(shape):
     # shapes where the plan takes held rows for a call with a per-tensor fp8 copy (the
-    # general 4-wavefront form); every row against the oracle
-    n, t, h, pd = shape
+    # general form, 4 or 8 wavefronts); every row against the oracle
+    n, t, h, pd, waves = shape
     ad = "f16" if pd == "f16" else "bf16"
     w = _case(n, t, h, pd, ad, 619, quant="per_tensor")
     plan = arf.arf_get_plan_quant(n, t, h, {"bf16": 0, "f16": 1, "f32": 2}[pd],
                                   arf.ARF_QUANT_PER_TENSOR)
-    assert plan["path"] == 3 and plan["waves"] == 4, plan
+    assert plan["path"] == 3 and plan["waves"] == waves, plan
     say("held rows, per-tensor copy, %s" % (shape,))
     (p, r, g), (pd_, rd, gd) = upload(w)
     ref = run_oracle(p, r, g, w.eps, pd, ad, quant="per_tensor", scale_in=0.03)
