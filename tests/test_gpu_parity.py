@@ -1045,6 +1045,26 @@ def test_held_rows_with_a_per_tensor_copy_every_row(shape):
     compare(run_gpu(pd_, rd, gd, w.eps, ad, quant="per_tensor", scale=0.03), ref,
             "per-tensor %s, held rows" % (shape,))
 
+
+@pytest.mark.parametrize("shape", [(8, 2048, 7168, "bf16", 8), (4, 2048, 8192, "f16", 8),
+                                   (16, 3072, 4096, "bf16", 8), (4, 2048, 7168, "bf16", 4)])
+def test_held_rows_forced_with_per_token_scales_every_row(shape):
+    # held rows forced on calls with a per-token copy: batches of several rows per
+    # workgroup, whose maxima are formed before any code is written; every row against
+    # the oracle
+    n, t, h, pd, waves = shape
+    ad = "f16" if pd == "f16" else "bf16"
+    w = _case(n, t, h, pd, ad, 620, quant="per_token")
+    say("held rows forced, per-token scales, %s" % (shape,))
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    ref = run_oracle(p, r, g, w.eps, pd, ad, quant="per_token")
+    try:
+        arf.arf_set_path_override(3, waves, 0)
+        got = run_gpu(pd_, rd, gd, w.eps, ad, quant="per_token")
+    finally:
+        arf.arf_set_path_override(0)
+    compare(got, ref, "held rows forced, per-token, %s" % (shape,))
+
 # ---- HIP graph capture --------------------------------------------------------------------
 
 @pytest.mark.parametrize("path", [0, 4])
