@@ -212,8 +212,10 @@ bool held_wins(int64_t tokens, int32_t hidden, int n, int quant, int pdt, const 
     if (quant == arf::kQuantTensor) {
         // A per-tensor fp8 copy takes the general form, where it measured faster than rows
         // by index (7 interleaved repetitions each; one shard was not faster throughout):
-        //  - fp32 partials, 4 wavefronts: 2-8 shards, hidden 6144-8192, from 4 rows per CU
-        //    (6 of 6 shapes 0.6-3.2% faster; hidden 4096-5120 and 3 rows per CU mixed);
+        //  - fp32 partials, 4 wavefronts, 2-8 shards: hidden 6144-8192 from 3 rows per CU
+        //    (16 of 16 shapes 0.3-9.4% faster) and hidden 4096 from 8 rows per CU (12 of
+        //    12, 1.1-9.3%); hidden 5120 (-2.3% to +5.9%) and 4096 at 3-4 rows per CU
+        //    (-4.3% to +1.9%) were mixed;
         //  - 16-bit partials, 2-4 shards, hidden 6144-8192, from 4 rows per CU: 4 wavefronts
         //    (10 of 10 shapes 2.8-9.1% faster; 4 x 2048 x 7168: 39.9 -> 36.5 us);
         //  - 16-bit partials otherwise 8 wavefronts: 2-4 shards below hidden 6144 (9 of 9,
@@ -221,9 +223,13 @@ bool held_wins(int64_t tokens, int32_t hidden, int n, int quant, int pdt, const 
         //    (9 of 10, 2.3-9.2%; one +0.6%); 9-16 shards at 3-4 rows per CU were mixed
         //    (-3.7% to +5.2%).
         if (n < 2 || tokens < (pdt != ARF_F32 && n > 8 ? 8LL : 3LL) * dev.cus) return false;
-        const bool four = pdt == ARF_F32 || (n <= 4 && hidden >= 6144);
-        if (four && (hidden < 6144 || n > 8 || tokens < 4LL * dev.cus)) return false;
-        eight = eight && !four;
+        if (pdt == ARF_F32) {
+            if (n > 8 || !(hidden >= 6144 || (hidden == 4096 && tokens >= 8LL * dev.cus)))
+                return false;
+        } else if (n <= 4 && hidden >= 6144) {
+            if (tokens < 4LL * dev.cus) return false;
+            eight = false;
+        }
     } else if (quant != arf::kQuantNone) {
         return false;
     }

@@ -229,13 +229,14 @@ def test_plan_with_a_quantised_copy():
     for q in (arf.ARF_QUANT_PER_TOKEN, arf.ARF_QUANT_MXFP4):
         assert qplan(4, 2048, 7168, q, 2)["path"] == 2
         assert qplan(2, 2048, 8192, q)["path"] != 3
-    # a per-tensor copy. fp32 partials: 2-8 shards, hidden 6144-8192, from 4 rows per CU,
-    # 4 wavefronts
+    # a per-tensor copy. fp32 partials: 4 wavefronts, 2-8 shards, hidden 6144-8192 from 3
+    # rows per CU, hidden 4096 from 8
     t = arf.ARF_QUANT_PER_TENSOR
     assert qplan(4, 2048, 7168, t, 2) == {"path": 3, "waves": 4, "chunks": 4, "grid": 256}
     assert qplan(8, 1536, 7168, t, 2)["path"] == 3 and qplan(9, 1536, 7168, t, 2)["path"] != 3
-    assert qplan(4, 2048, 4096, t, 2)["path"] != 3 and qplan(4, 1023, 8192, t, 2)["path"] != 3
-    assert qplan(1, 2048, 8192, t, 2)["path"] != 3
+    assert qplan(4, 768, 8192, t, 2)["path"] == 3 and qplan(4, 767, 8192, t, 2)["path"] != 3
+    assert qplan(4, 2047, 4096, t, 2)["path"] != 3 and qplan(4, 2048, 4096, t, 2)["path"] == 3
+    assert qplan(4, 2048, 5120, t, 2)["path"] != 3 and qplan(1, 2048, 8192, t, 2)["path"] != 3
     # 16-bit partials, 2-4 shards: hidden 6144-8192 from 4 rows per CU with 4 wavefronts,
     # below 6144 from 3 rows per CU with 8
     assert qplan(2, 2048, 8192, t) == {"path": 3, "waves": 4, "chunks": 4, "grid": 256}
