@@ -216,18 +216,18 @@ bool held_wins(int64_t tokens, int32_t hidden, int n, int quant, int pdt, const 
         //    (16 of 16 shapes 0.3-9.4% faster) and hidden 4096 from 8 rows per CU (12 of
         //    12, 1.1-9.3%); hidden 5120 (-2.3% to +5.9%) and 4096 at 3-4 rows per CU
         //    (-4.3% to +1.9%) were mixed;
-        //  - 16-bit partials, 2-4 shards, hidden 6144-8192, from 4 rows per CU: 4 wavefronts
-        //    (10 of 10 shapes 2.8-9.1% faster; 4 x 2048 x 7168: 39.9 -> 36.5 us);
-        //  - 16-bit partials otherwise 8 wavefronts: 2-4 shards below hidden 6144 (9 of 9,
-        //    2.3-6.8%), 5-8 shards (18 of 18, 0.4-7.9%) and 9-16 shards from 8 rows per CU
-        //    (9 of 10, 2.3-9.2%; one +0.6%); 9-16 shards at 3-4 rows per CU were mixed
-        //    (-3.7% to +5.2%).
+        //  - 16-bit partials, 2-4 shards, hidden 6144-8192, from 6 rows per CU: 4 wavefronts
+        //    (10 of 10 shapes 2.8-9.1% faster; 4 x 2048 x 7168: 39.9 -> 36.5 us; 8
+        //    wavefronts were -0.5% to +4.9% against 4 there);
+        //  - 16-bit partials otherwise 8 wavefronts: 2-4 shards at hidden 6144-8192 below 6
+        //    rows per CU (11 of 11, 0.3-13%), below hidden 6144 (9 of 9, 2.3-6.8%), 5-8 shards
+        //    (18 of 18, 0.4-7.9%) and 9-16 shards from 8 rows per CU (9 of 10, 2.3-9.2%; one
+        //    +0.6%); 9-16 shards at 3-4 rows per CU were mixed (-3.7% to +5.2%).
         if (n < 2 || tokens < (pdt != ARF_F32 && n > 8 ? 8LL : 3LL) * dev.cus) return false;
         if (pdt == ARF_F32) {
             if (n > 8 || !(hidden >= 6144 || (hidden == 4096 && tokens >= 8LL * dev.cus)))
                 return false;
-        } else if (n <= 4 && hidden >= 6144) {
-            if (tokens < 4LL * dev.cus) return false;
+        } else if (n <= 4 && hidden >= 6144 && tokens >= 6LL * dev.cus) {
             eight = false;
         }
     } else if (quant != arf::kQuantNone) {

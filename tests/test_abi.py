@@ -237,10 +237,11 @@ def test_plan_with_a_quantised_copy():
     assert qplan(4, 768, 8192, t, 2)["path"] == 3 and qplan(4, 767, 8192, t, 2)["path"] != 3
     assert qplan(4, 2047, 4096, t, 2)["path"] != 3 and qplan(4, 2048, 4096, t, 2)["path"] == 3
     assert qplan(4, 2048, 5120, t, 2)["path"] != 3 and qplan(1, 2048, 8192, t, 2)["path"] != 3
-    # 16-bit partials, 2-4 shards: hidden 6144-8192 from 4 rows per CU with 4 wavefronts,
-    # below 6144 from 3 rows per CU with 8
+    # 16-bit partials, 2-4 shards: hidden 6144-8192 from 6 rows per CU with 4 wavefronts,
+    # otherwise from 3 rows per CU with 8
     assert qplan(2, 2048, 8192, t) == {"path": 3, "waves": 4, "chunks": 4, "grid": 256}
-    assert qplan(4, 1023, 8192, t)["path"] != 3 and qplan(4, 1024, 8192, t)["path"] == 3
+    assert qplan(4, 1535, 8192, t) == {"path": 3, "waves": 8, "chunks": 2, "grid": 256}
+    assert qplan(4, 1536, 8192, t)["waves"] == 4 and qplan(4, 767, 8192, t)["path"] != 3
     assert qplan(4, 2048, 6144, t)["waves"] == 4 and qplan(4, 2048, 6136, t)["waves"] == 8
     assert qplan(4, 2048, 4096, t) == {"path": 3, "waves": 8, "chunks": 1, "grid": 256}
     assert qplan(3, 767, 4096, t)["path"] != 3 and qplan(3, 768, 4096, t)["path"] == 3

@@ -1026,8 +1026,8 @@ def test_held_rows_beyond_64_per_batch(pd, quant):
 
 
 
-@pytest.mark.parametrize("shape", [(4, 2048, 7168, "bf16", 4), (2, 1024, 8192, "f16", 4),
-                                   (8, 1536, 7168, "f32", 4), (3, 1024, 6144, "bf16", 4),
+@pytest.mark.parametrize("shape", [(4, 2048, 7168, "bf16", 4), (2, 1024, 8192, "f16", 8),
+                                   (8, 1536, 7168, "f32", 4), (3, 1536, 6144, "bf16", 4),
                                    (8, 2048, 7168, "bf16", 8), (3, 768, 4096, "f16", 8),
                                    (12, 2048, 4096, "bf16", 8), (6, 2048, 4096, "f32", 4),
                                    (2, 768, 7168, "f32", 4)])
