@@ -182,7 +182,9 @@ SURVEY_SHAPES = (
      for t in (1024, 4096, 16384)]
     + [(4, t, h, "f32", None) for h in (4096, 7168, 8192) for t in (2048, 8192)]
     + [(8, 4096, 8192, "bf16", "per_token"), (8, 8192, 16384, "bf16", "per_token"),
-       (8, 4096, 4096, "bf16", "per_token"), (4, 16384, 4096, "bf16", "per_token")])
+       (8, 4096, 4096, "bf16", "per_token"), (4, 16384, 4096, "bf16", "per_token")]
+    + [(4, 2048, 7168, "bf16", "per_tensor"), (8, 2048, 7168, "bf16", "per_tensor"),
+       (2, 1024, 8192, "bf16", "per_tensor"), (4, 2048, 7168, "f32", "per_tensor")])
 
 
 def survey(args, dev, stream):
