@@ -77,6 +77,8 @@ class Runner:
                      if w.quant == "per_tensor" else None)
             self.sets.append((p, r, g, rout, nout, q, sc_out, sc_in))
         self.k = 0
+        # the inputs are generated on the current stream; launches go to ``stream``
+        torch.cuda.synchronize()
 
     def step(self):
         import shard_reduce_residual_amd as arf
