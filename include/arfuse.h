@@ -254,6 +254,14 @@ arf_status arf_set_path_override(int32_t path, int32_t waves_per_block,
 arf_status arf_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream);
 
 /*
+ * The MXFP4 copy's element conversion alone, for testing it: out[i] = E2M1 code of in[i] in
+ * the low nibble (OCP MX FP4: round to nearest even over 0, 0.5, 1, 1.5, 2, 3, 4, 6,
+ * saturating to +-6, infinities and NaN to +-6, sign in bit 3), with no block scale. in and
+ * out are device pointers (in 4-byte aligned), n >= 0 elements. One kernel on `stream`.
+ */
+arf_status arf_e2m1_encode(const float* in, uint8_t* out, int64_t n, void* stream);
+
+/*
  * Streaming copy of `bytes` bytes (a multiple of 16; both pointers 16-byte aligned, the
  * ranges must not overlap) with the same load/store forms as the fused kernel: the
  * measured HBM ceiling and the calibration kernel for the byte counters.

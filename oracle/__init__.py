@@ -85,7 +85,8 @@ def lib() -> ctypes.CDLL:
         L.arfo_e2m1_to_f32.restype = f32
         L.arfo_mx_scale_code.argtypes = [f32]
         L.arfo_mx_scale_code.restype = ctypes.c_uint8
-        for name in ("arfo_f32_to_bf16_n", "arfo_f32_to_f16_n", "arfo_f32_to_e4m3_n"):
+        for name in ("arfo_f32_to_bf16_n", "arfo_f32_to_f16_n", "arfo_f32_to_e4m3_n",
+                     "arfo_f32_to_e2m1_n"):
             getattr(L, name).argtypes = [vp, vp, i64]
             getattr(L, name).restype = None
         L.arfo_reduce_add_rmsnorm.argtypes = [vp, i32, i64, i32, i32, i32, vp, vp, vp, f32,
@@ -137,9 +138,10 @@ def f32_to_e4m3(x) -> np.ndarray:
 
 
 def f32_to_e2m1(x) -> np.ndarray:
-    f = lib().arfo_f32_to_e2m1
     x = np.ascontiguousarray(x, dtype=np.float32)
-    return np.array([f(float(v)) for v in x.ravel()], np.uint8).reshape(x.shape)
+    out = np.empty(x.shape, np.uint8)
+    lib().arfo_f32_to_e2m1_n(_ptr(x), _ptr(out), x.size)
+    return out
 
 
 def mx_scale_code(amax) -> np.ndarray:

@@ -202,6 +202,11 @@ void arfo_f32_to_e4m3_n(const float* x, uint8_t* out, int64_t n)
     for (int64_t i = 0; i < n; ++i) out[i] = arfo_f32_to_e4m3(x[i]);
 }
 
+void arfo_f32_to_e2m1_n(const float* x, uint8_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = arfo_f32_to_e2m1(x[i]);
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* Element access.                                                                      */
 /* ------------------------------------------------------------------------------------ */

@@ -52,6 +52,7 @@ uint8_t  arfo_mx_scale_code(float amax);
 void arfo_f32_to_bf16_n(const float* x, uint16_t* out, int64_t n);
 void arfo_f32_to_f16_n(const float* x, uint16_t* out, int64_t n);
 void arfo_f32_to_e4m3_n(const float* x, uint8_t* out, int64_t n);
+void arfo_f32_to_e2m1_n(const float* x, uint8_t* out, int64_t n);
 
 /*
  * partials     [n_shards][tokens][hidden] of partial_dtype (ARFO_BF16/F16/F32)

@@ -50,6 +50,7 @@ SIGNATURES = {
     "arf_get_plan_quant": (_i32, [_i32, _i64, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32)]),
     "arf_set_path_override": (_i32, [_i32, _i32, _i32]),
     "arf_e4m3_encode": (_i32, [_vp, _vp, _i64, _vp]),
+    "arf_e2m1_encode": (_i32, [_vp, _vp, _i64, _vp]),
     "arf_stream_copy": (_i32, [_vp, _vp, _i64, _vp]),
     "arf_stream_mix": (_i32, [_vp, _i64, _vp, _i64, _i64, _vp]),
 }
@@ -269,6 +270,15 @@ def arf_e4m3_encode(x, out, stream=None) -> None:
     _check(lib().arf_e4m3_encode(_dev("x", x, dev, None, _types().f32),
                                  _dev("out", out, dev, x.numel(), _types().u8),
                                  x.numel(), _stream(stream)), "arf_e4m3_encode")
+
+
+def arf_e2m1_encode(x, out, stream=None) -> None:
+    dev = x.get_device()
+    if dev < 0:
+        raise ValueError("x must be a device tensor (got %s)" % x.device)
+    _check(lib().arf_e2m1_encode(_dev("x", x, dev, None, _types().f32),
+                                 _dev("out", out, dev, x.numel(), _types().u8),
+                                 x.numel(), _stream(stream)), "arf_e2m1_encode")
 
 
 def _bytes_at_least(name, t, nbytes):

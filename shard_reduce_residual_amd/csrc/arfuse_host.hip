@@ -610,6 +610,22 @@ __global__ __launch_bounds__(256) void e4m3_encode_kernel(const float* __restric
     }
 }
 
+// One E2M1 code per byte (the low nibble), through the MXFP4 store's conversion.
+__global__ __launch_bounds__(256) void e2m1_encode_kernel(const float* __restrict__ in,
+                                                          uint8_t* __restrict__ out,
+                                                          int64_t n) {
+    for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n;
+         i += (int64_t)gridDim.x * 256 * 4) {
+        float v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = i + k < n ? in[i + k] : 0.0f;
+        const uint32_t w = arf::e2m1_pack4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (i + k < n) out[i + k] = (uint8_t)((w >> (4 * k)) & 0xFu);
+    }
+}
+
 // Contiguous spans of 256 lanes x 8 x 16 bytes per workgroup iteration, through a buffer
 // resource per span (the fused kernel's load/store forms, non-temporal).
 constexpr int kCopyUnroll = 8;
@@ -826,6 +842,21 @@ arf_status arf_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* strea
     const int64_t blocks = std::min<int64_t>((n + 1023) / 1024, (int64_t)UINT32_MAX / 256);
     void* args[] = {&in, &out, &n};
     return hipLaunchKernel(reinterpret_cast<const void*>(&e4m3_encode_kernel),
+                           dim3((uint32_t)blocks), dim3(256), args, 0,
+                           (hipStream_t)stream) == hipSuccess
+               ? ARF_OK
+               : ARF_ERR_HIP;
+}
+
+arf_status arf_e2m1_encode(const float* in, uint8_t* out, int64_t n, void* stream) {
+    if (n < 0) return ARF_ERR_SHAPE;
+    if (n == 0) return ARF_OK;
+    if (!in || !out) return ARF_ERR_NULL;
+    if (!aligned(in, 4)) return ARF_ERR_ALIGN;
+    if (overlap(span(in, n * 4), span(out, n))) return ARF_ERR_ALIAS;
+    const int64_t blocks = std::min<int64_t>((n + 1023) / 1024, (int64_t)UINT32_MAX / 256);
+    void* args[] = {&in, &out, &n};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&e2m1_encode_kernel),
                            dim3((uint32_t)blocks), dim3(256), args, 0,
                            (hipStream_t)stream) == hipSuccess
                ? ARF_OK

@@ -102,6 +102,10 @@ int main() {
     EXPECT(arf_e4m3_encode(nullptr, Q, 0, nullptr) == ARF_OK);
     EXPECT(arf_e4m3_encode(nullptr, Q, 4, nullptr) == ARF_ERR_NULL);
     EXPECT(arf_e4m3_encode(reinterpret_cast<float*>(base + 2), Q, 4, nullptr) == ARF_ERR_ALIGN);
+    EXPECT(arf_e2m1_encode(nullptr, Q, -1, nullptr) == ARF_ERR_SHAPE);
+    EXPECT(arf_e2m1_encode(nullptr, Q, 0, nullptr) == ARF_OK);
+    EXPECT(arf_e2m1_encode(nullptr, Q, 4, nullptr) == ARF_ERR_NULL);
+    EXPECT(arf_e2m1_encode(reinterpret_cast<float*>(base + 2), Q, 4, nullptr) == ARF_ERR_ALIGN);
     EXPECT(arf_stream_copy(RO, P, 24, nullptr) == ARF_ERR_SHAPE);
     EXPECT(arf_stream_copy(P, base + 16, 64, nullptr) == ARF_ERR_ALIAS);
     EXPECT(arf_stream_mix(nullptr, 0, nullptr, 0, 0, nullptr) == ARF_OK);

@@ -27,7 +27,7 @@ def declared_symbols():
 def test_library_exports_every_declared_symbol():
     L = arf.lib()
     names = declared_symbols()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(arf.SIGNATURES)
@@ -117,6 +117,11 @@ def test_utility_entry_point_validation():
     assert L.arf_e4m3_encode(P, Q, -1, None) == SHAPE
     assert L.arf_e4m3_encode(P + 2, Q, 8, None) == ALIGN
     assert L.arf_e4m3_encode(P, P + 4, 8, None) == ALIAS
+    assert L.arf_e2m1_encode(P, Q, 0, None) == OK
+    assert L.arf_e2m1_encode(None, Q, 8, None) == NULL
+    assert L.arf_e2m1_encode(P, Q, -1, None) == SHAPE
+    assert L.arf_e2m1_encode(P + 2, Q, 8, None) == ALIGN
+    assert L.arf_e2m1_encode(P, P + 4, 8, None) == ALIAS
     assert L.arf_stream_copy(Q, P, 0, None) == OK
     assert L.arf_stream_copy(Q, P, 24, None) == SHAPE
     assert L.arf_stream_copy(Q, None, 32, None) == NULL

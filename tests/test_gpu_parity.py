@@ -557,6 +557,43 @@ def test_e4m3_conversion_matches_the_oracle():
     assert np.array_equal(e4m3_brute(pts[:4096]), want[:4096])
 
 
+def _e2m1_gpu(x):
+    xd = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    out = torch.empty(xd.numel(), dtype=torch.uint8, device=DEV)
+    arf.arf_e2m1_encode(xd, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_e2m1_conversion_matches_the_oracle():
+    # the MXFP4 store's element conversion (gfx950's packed fp32 -> fp4 instruction) on
+    # every fp32 value of magnitude 2^-4 to 8, both signs: every rounding boundary of E2M1,
+    # its ties and the saturation at 6; then zeros, subnormals, infinities, NaN (with its
+    # sign) and random patterns of every magnitude
+    say("e2m1 encoder")
+    mant = np.arange(1 << 23, dtype=np.uint32)
+    for e in range(123, 130):
+        for sign in (0, 0x80000000):
+            x = (mant | np.uint32((e << 23) | sign)).view(np.float32)
+            got, want = _e2m1_gpu(x), oracle.f32_to_e2m1(x)
+            bad = np.nonzero(got != want)[0]
+            assert bad.size == 0, [(hex(int(x.view(np.uint32)[i])), int(got[i]), int(want[i]))
+                                   for i in bad[:10]]
+    rng = np.random.default_rng(4)
+    x = np.concatenate([
+        rng.integers(0, 2 ** 32, 1 << 22, dtype=np.uint64).astype(np.uint32).view(np.float32),
+        rng.integers(0, 1 << 23, 1 << 16, dtype=np.uint32).view(np.float32),   # subnormals
+        np.array([0.0, -0.0, np.inf, -np.inf, np.nan, -np.nan, 6.0, -6.0, 1e30, -1e30],
+                 np.float32)])
+    assert np.array_equal(_e2m1_gpu(x), oracle.f32_to_e2m1(x))
+    # odd length: the tail is converted and nothing past it is written
+    y = torch.from_numpy(x[:1001]).to(DEV)
+    o2 = torch.full((1001 + 64,), 0x5A, dtype=torch.uint8, device=DEV)
+    arf.arf_e2m1_encode(y, o2[:1001])
+    torch.cuda.synchronize()
+    o2 = o2.cpu().numpy()
+    assert np.array_equal(o2[:1001], oracle.f32_to_e2m1(x[:1001])) and np.all(o2[1001:] == 0x5A)
+
 def test_stream_copy_is_exact():
     for nbytes in (16, 4096 + 48, 3 * 32768 + 16, 64 << 20):
         say("stream copy %d bytes" % nbytes)
