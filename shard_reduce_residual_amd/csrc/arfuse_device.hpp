@@ -127,10 +127,11 @@ __device__ __forceinline__ u32x4 pack8(ActF16, const float f[8]) {
 }
 
 // ---- fp32 -> OCP E4M3 ------------------------------------------------------------------
-// Magnitudes above 448 are clamped first (saturating conversion; NaN is kept), then the
-// hardware converter rounds to nearest even. Four values -> one dword, lowest byte first.
+// Magnitudes above 448 are clamped first (saturating conversion; NaN is kept), with one
+// median-of-three, then the hardware converter rounds to nearest even. Four values -> one
+// dword, lowest byte first.
 __device__ __forceinline__ float e4m3_sat(float v) {
-    float c = __builtin_fabsf(v) <= 448.0f ? v : __builtin_copysignf(448.0f, v);
+    const float c = __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
     return v != v ? v : c;
 }
 
