@@ -216,6 +216,11 @@ static void cpu_checks(void) {
     int32_t plan[4] = {0, 0, 0, 0};
     CHECK(arf_get_plan(8, 8192, 16384, ARF_BF16, 256, plan) == ARF_OK && plan[0] == 4, "plan of 8 x 8192 x 16384");
     CHECK(arf_get_plan(8, 8192, 2048, ARF_BF16, 256, plan) == ARF_OK && plan[0] == 4, "plan of 8 x 8192 x 2048");
+    CHECK(arf_get_plan_quant(4, 2048, 7168, ARF_F32, ARF_QUANT_PER_TENSOR, 256, plan) == ARF_OK && plan[0] == 3, "per-tensor plan of 4 x 2048 x 7168");
+    CHECK(arf_get_plan_quant(4, 2048, 7168, ARF_F32, ARF_QUANT_PER_TOKEN, 256, plan) == ARF_OK && plan[0] == 2, "per-token plan of 4 x 2048 x 7168");
+    CHECK(arf_get_plan_quant(4, 2048, 7168, ARF_F32, ARF_QUANT_NONE, 256, plan) == ARF_OK && plan[0] == 3, "plan without a copy");
+    CHECK(arf_get_plan_quant(4, 2048, 7168, ARF_F32, 9, 256, plan) == ARF_ERR_VALUE, "plan with copy mode 9");
+    CHECK(arf_e2m1_encode(NULL, NULL, 0, NULL) == ARF_OK, "empty e2m1 conversion");
 }
 
 int main(int argc, char** argv) {
