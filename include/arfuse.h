@@ -223,8 +223,8 @@ arf_status arf_get_plan(int32_t n_shards, int64_t tokens, int32_t hidden,
  * The same for a call with the quantised copy `quant_mode` (ARF_QUANT_NONE, which gives
  * arf_get_plan's answer, ARF_QUANT_PER_TENSOR, ARF_QUANT_PER_TOKEN or ARF_QUANT_MXFP4; any
  * other value: ARF_ERR_VALUE; MXFP4 with hidden % 32 != 0: ARF_ERR_SHAPE). The plan depends on
- * the copy where the held rows (path 3) are concerned: they take no per-token or MXFP4 copy,
- * and a per-tensor one in most of their range, with 4 or 8 wavefronts by shard count.
+ * the copy where the held rows (path 3) are concerned: they take no per-token copy, and a
+ * per-tensor or MXFP4 one in most of their range.
  */
 arf_status arf_get_plan_quant(int32_t n_shards, int64_t tokens, int32_t hidden,
                               int32_t partial_dtype, int32_t quant_mode, int32_t num_cus,

@@ -230,10 +230,16 @@ def test_plan_with_a_quantised_copy():
     # the plan of a call with a copy: ARF_QUANT_NONE is arf_get_plan's answer
     for args in [(4, 2048, 7168, 2), (8, 8192, 16384, 0), (2, 16, 1024, 0), (8, 64, 8192, 0)]:
         assert qplan(*args[:3], arf.ARF_QUANT_NONE, args[3]) == plan(*args)
-    # held rows take no per-token or MXFP4 copy
-    for q in (arf.ARF_QUANT_PER_TOKEN, arf.ARF_QUANT_MXFP4):
-        assert qplan(4, 2048, 7168, q, 2)["path"] == 2
-        assert qplan(2, 2048, 8192, q)["path"] != 3
+    # held rows take no per-token copy
+    assert qplan(4, 2048, 7168, arf.ARF_QUANT_PER_TOKEN, 2)["path"] == 2
+    assert qplan(2, 2048, 8192, arf.ARF_QUANT_PER_TOKEN)["path"] != 3
+    # an MXFP4 copy: the region without a copy, 9-16 16-bit shards from 8 rows per CU
+    m = arf.ARF_QUANT_MXFP4
+    assert qplan(4, 2048, 7168, m, 2) == plan(4, 2048, 7168, 2)
+    assert qplan(2, 2048, 8192, m) == {"path": 3, "waves": 8, "chunks": 2, "grid": 256}
+    assert qplan(8, 768, 4096, m)["path"] == 3 and qplan(8, 767, 4096, m)["path"] != 3
+    assert qplan(16, 2047, 4096, m)["path"] != 3 and qplan(16, 2048, 4096, m)["path"] == 3
+    assert qplan(1, 2048, 8192, m)["path"] == 3
     # a per-tensor copy. fp32 partials: 4 wavefronts, 2-8 shards, hidden 6144-8192 from 3
     # rows per CU, hidden 4096 from 8
     t = arf.ARF_QUANT_PER_TENSOR

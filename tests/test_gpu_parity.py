@@ -778,6 +778,23 @@ def test_mxfp4_every_geometry(pd):
         arf.arf_set_path_override(0)
 
 
+
+@pytest.mark.parametrize("shape", [(2, 2048, 8192, "bf16", 8), (6, 2048, 7168, "f32", 4),
+                                   (16, 2048, 4096, "bf16", 8), (3, 768, 8192, "f16", 8)])
+def test_mxfp4_on_held_rows_every_row(shape):
+    # shapes where the plan takes held rows for a call with an MXFP4 copy; every row against
+    # the oracle
+    n, t, h, pd, waves = shape
+    ad = "f16" if pd == "f16" else "bf16"
+    w = _case(n, t, h, pd, ad, 621, std=3.0)
+    plan = arf.arf_get_plan_quant(n, t, h, {"bf16": 0, "f16": 1, "f32": 2}[pd],
+                                  arf.ARF_QUANT_MXFP4)
+    assert plan["path"] == 3 and plan["waves"] == waves, plan
+    say("mxfp4 on held rows %s" % (shape,))
+    (p, r, g), (pd_, rd, gd) = upload(w)
+    ref = run_oracle(p, r, g, w.eps, pd, ad, quant="mxfp4")
+    compare_mx(run_gpu_mx(pd_, rd, gd, w.eps, ad), ref, "mxfp4 held %s" % (shape,))
+
 def test_mxfp4_zero_rows_and_full_size():
     say("mxfp4 zero rows")
     h = 2048
